@@ -1,0 +1,532 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every check here is independent of the oracle's own formulas: closed forms
+(Sylvester/Kronecker Hadamard, exact rational rounding with ``fractions``),
+brute force on tiny inputs, invariants the pages state, and constants the
+pages print (``tests/golden``). A plausible slip in the oracle -- a dropped
+butterfly stage, a wrong sign, a swapped nibble, a mis-rounded tie, a wrong
+scale rule, a transposed operand -- fails at least one of them.
+
+Pages: [P1] "Pretraining Large Language Models with MXFP4 on Native FP4
+Hardware" (arXiv:2605.09825 summary); [P2] FP4 training article on
+arXiv:2501.17116; [P3] "Decomposing MXFP4 quantization error" blog
+(arXiv:2605.20402).
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synthetic
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_table(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line.split())
+    return rows
+
+
+def sylvester(h):
+    """Natural-order Sylvester matrix by Kronecker powers of [[1,1],[1,-1]]."""
+    H = np.array([[1.0]])
+    while H.shape[0] < h:
+        H = np.kron(np.array([[1.0, 1.0], [1.0, -1.0]]), H)
+    return H
+
+
+def all_bf16_f32(finite_only=True):
+    bits = np.arange(65536, dtype=np.uint32)
+    v = (bits << 16).view(np.float32)
+    return v[np.isfinite(v)] if finite_only else v
+
+
+# ---------------------------------------------------------------- (a) H H^T = I
+def test_h16_rows_are_sylvester_and_orthonormal_bit_exact():
+    """[P1] quick-read block and section C: H H^T = I, H a +-1 (scaled) matrix."""
+    H = O.hadamard_rotate(np.eye(16, dtype=np.float32), 16)
+    assert H.dtype == np.float32
+    assert np.array_equal(H.astype(np.float64), sylvester(16) / 4.0)
+    # products are +-1/16 and 16-term sums are exact: bit-exact identity
+    HHt = np.zeros((16, 16), dtype=np.float32)
+    for i in range(16):
+        for j in range(16):
+            acc = np.float32(0)
+            for k in range(16):
+                acc = np.float32(acc + H[i, k] * H[j, k])
+            HHt[i, j] = acc
+    assert np.array_equal(HHt, np.eye(16, dtype=np.float32))
+
+
+def test_h32_orthonormal_to_rounding_only():
+    """H32's 1/sqrt(32) is irrational: H H^T = I holds to ~1e-7, not exactly."""
+    H = O.hadamard_rotate(np.eye(32, dtype=np.float32), 32).astype(np.float64)
+    c = float(np.float32(2.0 ** -2.5))
+    assert np.array_equal(H, sylvester(32) * c)
+    err = np.abs(H @ H.T - np.eye(32)).max()
+    assert 0 < err < 1e-6
+
+
+def test_butterfly_exact_on_small_integers():
+    """Small integers keep every fp32 add exact, so the butterfly equals x H."""
+    rng = np.random.default_rng(11)
+    x = rng.integers(-1024, 1025, size=(64, 128)).astype(np.float32)
+    for h in (16, 32):
+        y = O.hadamard_rotate(x, h).astype(np.float64)
+        H = sylvester(h) * (0.25 if h == 16 else float(np.float32(2.0 ** -2.5)))
+        ref = (x.astype(np.float64).reshape(64, 128 // h, h) @ H).reshape(64, 128)
+        if h == 16:
+            assert np.array_equal(y, ref)
+        else:  # one extra fp32 rounding in the final multiply
+            assert np.allclose(y, ref, rtol=2 ** -23, atol=0)
+
+
+def test_rotation_is_blockwise_and_aligned():
+    """Tiled layout ([P1] A.2): groups of h aligned at 0, no mixing across groups."""
+    x = np.zeros((1, 64), dtype=np.float32)
+    x[0, 17] = 1.0
+    y = O.hadamard_rotate(x, 16)
+    assert np.count_nonzero(y[0, :16]) == 0 and np.count_nonzero(y[0, 32:]) == 0
+    assert np.array_equal(y[0, 16:32].astype(np.float64), sylvester(16)[1] / 4.0)
+    assert np.array_equal(O.hadamard_rotate(x, 0), x)
+
+
+# ------------------------------------------------------------ (b) cancellation
+@pytest.mark.parametrize("op", ["fprop", "dgrad", "wgrad"])
+@pytest.mark.parametrize("h", [16, 32])
+def test_cancellation_identities(op, h):
+    """[P1] C.1-C.3: rotating both operands along the reduction axis leaves
+    the product unchanged (H H^T = I)."""
+    rng = np.random.default_rng(5)
+    T, N, K = 256, 96, 128
+    if op == "fprop":
+        P = synthetic.f64_to_bf16_bits(rng.normal(size=(T, K)))
+        Q = synthetic.f64_to_bf16_bits(rng.normal(size=(N, K)))
+    elif op == "dgrad":
+        P = synthetic.f64_to_bf16_bits(rng.normal(size=(T, N)))
+        Q = synthetic.f64_to_bf16_bits(rng.normal(size=(N, K)))
+    else:
+        P = synthetic.f64_to_bf16_bits(rng.normal(size=(T, N)))
+        Q = synthetic.f64_to_bf16_bits(rng.normal(size=(T, K)))
+    ref = O.unquantized_product(op, P, Q)
+    rot = O.rotated_unquantized_product(op, P, Q, h)
+    rel = np.linalg.norm(rot - ref) / np.linalg.norm(ref)
+    assert rel <= 1e-5
+    # and the rotation really changed the operands (not a no-op)
+    if op == "fprop":
+        assert not np.array_equal(O.hadamard_rotate(O.bf16_to_f32(P), h), O.bf16_to_f32(P))
+
+
+def test_cancellation_tiny_workload():
+    w = synthetic.make("tiny")
+    ref = O.unquantized_product("fprop", w["X"], w["W"])
+    rot = O.rotated_unquantized_product("fprop", w["X"], w["W"], 16)
+    assert np.linalg.norm(rot - ref) / np.linalg.norm(ref) <= 1e-5
+
+
+# --------------------------------------------------- (c) grid and saturation
+def test_grid_matches_pages():
+    """All 16 codes at scale byte 127 dequantize to the printed grid."""
+    table = {int(c): float(v) for c, v in _golden_table("e2m1_grid.txt")}
+    assert sorted(table) == list(range(8))
+    nib = np.array([[c | (c + 1) << 4 for c in range(0, 16, 2)] * 2], dtype=np.uint8)
+    vals = O.dequantize(nib, np.array([[127]], dtype=np.uint8))[0, :16]
+    for code in range(16):
+        want = table[code & 7] * (-1.0 if code & 8 else 1.0)
+        assert vals[code] == want
+        assert math.copysign(1.0, vals[code]) == (-1.0 if code & 8 else 1.0)
+    assert max(table.values()) == 6.0  # range +-6 ([P2] section 1)
+
+
+def test_saturation_at_six():
+    for v in (6.0, 6.5, 7.99, 1e30, np.inf):
+        assert O.e2m1_code(np.array([v], np.float32), np.array([0]))[0] == 7
+        assert O.e2m1_code(np.array([-v], np.float32), np.array([0]))[0] == 15
+
+
+_GRID_Q = [Fraction(g) for g in (0, 0.5, 1, 1.5, 2, 3, 4, 6)]
+
+
+def _nearest_code_exact(v: Fraction) -> int:
+    """Nearest grid value by exact distance; ties to the even code; clamp at 6."""
+    a = abs(v)
+    if a >= 6:
+        return 7
+    return min(range(8), key=lambda c: (abs(a - _GRID_Q[c]), c & 1))
+
+
+def test_e2m1_exhaustive_against_exact_rounding():
+    """Every finite bf16 value, at several shared exponents, against an
+    independent exact-arithmetic nearest-value rule."""
+    v = all_bf16_f32()
+    for E in (0, -3, 2, 5):
+        codes = O.e2m1_code(v, np.full(v.shape, E))
+        for x, c in zip(v.tolist(), codes.tolist()):
+            want = _nearest_code_exact(Fraction(x) / Fraction(2) ** E)
+            if math.copysign(1.0, x) < 0:
+                want |= 8
+            assert c == want, (x, E, c, want)
+
+
+def test_e2m1_tie_cases_round_to_even_code():
+    ties = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6}
+    for t, code in ties.items():
+        assert O.e2m1_code(np.array([t], np.float32), np.array([0]))[0] == code
+        assert O.e2m1_code(np.array([-t], np.float32), np.array([0]))[0] == code | 8
+
+
+# --------------------------------------------------------- E8M0 scale rules
+def _e_floor_exact(mb: Fraction) -> int:
+    """Largest E with 4 * 2^E <= m_b (max exponent minus emax = 2)."""
+    E = 200
+    while Fraction(4) * Fraction(2) ** E > mb:
+        E -= 1
+    return E
+
+
+def _e_ceil_exact(mb: Fraction) -> int:
+    """Smallest E with 6 * 2^E >= m_b ([P3]: ceiling of s* = m_b / 6)."""
+    E = -300
+    while Fraction(6) * Fraction(2) ** E < mb:
+        E += 1
+    return E
+
+
+def test_e8m0_exhaustive_over_bf16_amax():
+    v = all_bf16_f32()
+    v = v[v > 0]
+    Ef = O.e8m0_exponent(v, O.MODE_OCP_FLOOR)
+    Ec = O.e8m0_exponent(v, O.MODE_CEIL)
+    # coarse bisection keeps the exact search fast
+    for x, ef, ec in zip(v.tolist(), Ef.tolist(), Ec.tolist()):
+        mb = Fraction(x)
+        wf = max(-127, min(127, _e_floor_exact_fast(mb)))
+        wc = max(-127, min(127, _e_ceil_exact_fast(mb)))
+        assert ef == wf, (x, ef, wf)
+        assert ec == wc, (x, ec, wc)
+
+
+def _e_floor_exact_fast(mb):
+    E = mb.numerator.bit_length() - mb.denominator.bit_length() - 2 + 2
+    while Fraction(4) * Fraction(2) ** E > mb:
+        E -= 1
+    while Fraction(4) * Fraction(2) ** (E + 1) <= mb:
+        E += 1
+    return E
+
+
+def _e_ceil_exact_fast(mb):
+    E = mb.numerator.bit_length() - mb.denominator.bit_length() - 4
+    while Fraction(6) * Fraction(2) ** E < mb:
+        E += 1
+    while Fraction(6) * Fraction(2) ** (E - 1) >= mb:
+        E -= 1
+    return E
+
+
+def test_e8m0_search_helpers_agree_with_plain_search():
+    for x in (1.0, 1.5, 1.50390625, 6.0, 7.0, 2.0 ** -130, 3.0e38, 0.1):
+        mb = Fraction(x)
+        assert _e_floor_exact_fast(mb) == _e_floor_exact(mb)
+        assert _e_ceil_exact_fast(mb) == _e_ceil_exact(mb)
+
+
+def test_scale_bracket():
+    """ceil: 1 <= 2^E / (m_b / 6) < 2 ([P3] scale-bias section, gamma = 2^delta);
+    floor: 4 * 2^E <= m_b < 8 * 2^E (block max lands in [4, 8) after scaling).
+    Over every positive finite bf16 m_b above the E clamp."""
+    v = all_bf16_f32()
+    v = v[(v > 0) & (v >= 2.0 ** -124)].astype(np.float64)
+    Ec = O.e8m0_exponent(v, O.MODE_CEIL)
+    gamma = np.ldexp(1.0, Ec) / (v / 6.0)
+    assert np.all(gamma >= 1.0) and np.all(gamma < 2.0)
+    Ef = O.e8m0_exponent(v, O.MODE_OCP_FLOOR)
+    assert np.all(np.ldexp(4.0, Ef) <= v) and np.all(v < np.ldexp(8.0, Ef))
+    assert O.e8m0_exponent(np.array([0.0]), O.MODE_CEIL)[0] == -127
+    assert O.e8m0_exponent(np.array([0.0]), O.MODE_OCP_FLOOR)[0] == -127
+
+
+def test_mean_gamma_is_one_over_ln2():
+    """[P3] scale-bias section: gamma = 2^delta, delta ~ U[0, 1), about 44%
+    average overshoot; E[2^delta] = 1/ln 2."""
+    consts = dict(_golden_table("format_constants.txt"))
+    rng = np.random.default_rng(7)
+    m_b = np.exp2(rng.uniform(0, 20, size=400_000)).astype(np.float32)
+    E = O.e8m0_exponent(m_b, O.MODE_CEIL)
+    gamma = np.ldexp(1.0, E) / (m_b.astype(np.float64) / 6.0)
+    assert abs(gamma.mean() - 1 / math.log(2)) < 4e-3
+    assert round(100 * (gamma.mean() - 1)) == int(consts["gamma_mean_excess_percent"])
+
+
+# ------------------------------------------------- whole-block scalar encoder
+def _encode_block_exact(y32, mode):
+    """Independent scalar encoder of one 32-element fp32 block with exact
+    rationals: returns (scale byte, list of codes)."""
+    vals = [Fraction(float(t)) for t in y32]
+    mb = max(abs(t) for t in vals)
+    if mb == 0:
+        E = -127
+    else:
+        E = _e_floor_exact_fast(mb) if mode == O.MODE_OCP_FLOOR else _e_ceil_exact_fast(mb)
+        E = max(-127, min(127, E))
+    codes = []
+    for t, f in zip(vals, y32):
+        c = _nearest_code_exact(t / Fraction(2) ** E)
+        if math.copysign(1.0, float(f)) < 0:
+            c |= 8
+        codes.append(c)
+    return E + 127, codes
+
+
+def _reference_quantize_scalar(src_bits, axis, h, mode):
+    """Loops over blocks with the scalar encoder, rotating with the explicit
+    Sylvester matrix product (fp64 exact on these inputs, then fp32)."""
+    x = synthetic.bf16_bits_to_f32(src_bits).astype(np.float64)
+    if axis == O.AXIS_COL:
+        x = x.T
+    R, C = x.shape
+    if h:
+        H = sylvester(h) * (0.25 if h == 16 else float(np.float32(2.0 ** -2.5)))
+        x = (x.reshape(R, C // h, h) @ H).reshape(R, C)
+    y = x.astype(np.float32)
+    codes = np.zeros((R, C), dtype=np.uint8)
+    if axis == O.AXIS_2D:
+        sc = np.zeros((R // 32, C // 32), dtype=np.uint8)
+        for bi in range(R // 32):
+            for bj in range(C // 32):
+                tile = y[bi * 32:(bi + 1) * 32, bj * 32:(bj + 1) * 32].ravel()
+                s, cs = _encode_block_exact(tile, mode)
+                sc[bi, bj] = s
+                codes[bi * 32:(bi + 1) * 32, bj * 32:(bj + 1) * 32] = np.array(cs).reshape(32, 32)
+    else:
+        sc = np.zeros((R, C // 32), dtype=np.uint8)
+        for i in range(R):
+            for b in range(C // 32):
+                s, cs = _encode_block_exact(y[i, b * 32:(b + 1) * 32], mode)
+                sc[i, b] = s
+                codes[i, b * 32:(b + 1) * 32] = cs
+    nib = np.zeros((R, C // 2), dtype=np.uint8)
+    for j in range(C // 2):
+        nib[:, j] = codes[:, 2 * j] | (codes[:, 2 * j + 1] << 4)
+    return nib, sc
+
+
+@pytest.mark.parametrize("axis", [O.AXIS_ROW, O.AXIS_COL, O.AXIS_2D])
+@pytest.mark.parametrize("mode", [O.MODE_OCP_FLOOR, O.MODE_CEIL])
+@pytest.mark.parametrize("h", [0, 16])
+def test_oracle_matches_scalar_exact_encoder(axis, mode, h):
+    """Small integer-valued inputs make the fp64 matrix rotation exact, so the
+    scalar encoder sees the same fp32 values as the butterfly."""
+    rng = np.random.default_rng(100 + axis * 10 + mode * 3 + h)
+    base = rng.integers(-64, 65, size=(64, 96)).astype(np.float64)
+    base *= np.exp2(rng.integers(-3, 4, size=(1, 96)))
+    src = synthetic.f64_to_bf16_bits(base)
+    nib, sc = O.quantize(src, axis, h, mode)
+    rnib, rsc = _reference_quantize_scalar(src, axis, h, mode)
+    assert np.array_equal(sc, rsc)
+    assert np.array_equal(nib, rnib)
+
+
+def test_oracle_matches_scalar_encoder_heavy_tails():
+    """Student-t data (the quantizer workload's distribution), no rotation,
+    both modes, row axis."""
+    a = synthetic.make("quant", scale=512)["A"][:, :256]
+    for mode in (O.MODE_OCP_FLOOR, O.MODE_CEIL):
+        nib, sc = O.quantize(a, O.AXIS_ROW, 0, mode)
+        rnib, rsc = _reference_quantize_scalar(a, O.AXIS_ROW, 0, mode)
+        assert np.array_equal(sc, rsc) and np.array_equal(nib, rnib)
+
+
+def test_reconstruction_error_bound_and_positions():
+    """x_rec = 2^E Q(x / 2^E) ([P1] A.1): every element's reconstruction is
+    within half a grid gap of its input (gaps 0.5, 1, 2 on [0,2], [2,4],
+    [4,6]; saturated values lose |v| - 6); a swapped nibble or a misplaced
+    scale breaks this on random data."""
+    rng = np.random.default_rng(3)
+    src = synthetic.f64_to_bf16_bits(rng.standard_t(3, size=(64, 256)))
+    for axis in (O.AXIS_ROW, O.AXIS_COL, O.AXIS_2D):
+        for mode in (O.MODE_OCP_FLOOR, O.MODE_CEIL):
+            nib, sc = O.quantize(src, axis, 16, mode)
+            deq = O.dequantize(nib, sc, two_d=(axis == O.AXIS_2D))
+            x = O.bf16_to_f32(src)
+            y = O.hadamard_rotate(x.T if axis == O.AXIS_COL else x, 16).astype(np.float64)
+            if axis == O.AXIS_2D:
+                scale = np.repeat(np.repeat(np.ldexp(1.0, sc.astype(int) - 127), 32, 0), 32, 1)
+            else:
+                scale = np.repeat(np.ldexp(1.0, sc.astype(int) - 127), 32, 1)
+            assert deq.shape == y.shape
+            err = np.abs(deq - y)
+            a = np.abs(y) / scale
+            half_gap = np.select([a <= 2, a <= 4, a <= 6], [0.25, 0.5, 1.0], a - 6)
+            assert np.all(err <= half_gap * scale)
+
+
+# ------------------------------------------------------------- (d) deadzone
+def test_deadzone_rule():
+    """[P3] core insight: |x| < m_b / 24 is the deadzone. Ideal scale: such
+    x quantize to 0 under Q*; with the ceiling scale (s_b >= s*) also under Q.
+    With either mode, a scaled magnitude <= 1/4 is exactly code 0."""
+    consts = dict(_golden_table("format_constants.txt"))
+    div = int(consts["deadzone_divisor"])
+    assert div == 4 * int(consts["q_max"])  # m_b/24 = s* * (q_min / 2), q_min = 0.5
+    a = synthetic.make("quant", scale=64)["A"]
+    x = O.hadamard_rotate(O.bf16_to_f32(a), 16)
+    blocks = x.reshape(-1, 32)
+    for mode in (O.MODE_OCP_FLOOR, O.MODE_CEIL):
+        d = O.error_decomposition(blocks, mode)
+        dz = div * np.abs(blocks.astype(np.float64)) < d["m_b"].astype(np.float64)[:, None]
+        assert np.array_equal(dz, d["deadzone"])
+        assert np.all(d["Q_star"][dz] == 0)
+        if mode == O.MODE_CEIL:
+            assert np.all(d["Q"][dz] == 0)
+        codes = O.e2m1_code(blocks, d["E"][:, None])
+        v = np.abs(np.ldexp(blocks.astype(np.float64), -d["E"][:, None]))
+        assert np.array_equal((codes & 7) == 0, v <= 0.25)
+
+
+# ------------------------------------------------------- (e) orthogonality
+def _pair_blocks():
+    v = all_bf16_f32()
+    v = v[(v >= 2.0 ** -4) & (v <= 2.0 ** 4)]
+    a = np.repeat(v, v.size)
+    x = np.tile(v, v.size)
+    blocks = np.zeros((a.size, 32), dtype=np.float32)
+    blocks[:, 0] = a
+    blocks[:, 1] = x
+    return blocks
+
+
+def test_orthogonality_bruteforce_pairs():
+    """[P3] Property 1: <e_DZ, e_scale> = <e_DZ, e_grid> = 0, pointwise, under
+    the ceiling scale. Every block {a, x, 0 x 30} with a, x over all bf16
+    values in [2^-4, 2^4] (covers every deadzone edge)."""
+    blocks = _pair_blocks()
+    assert blocks.shape[0] > 1_000_000
+    d = O.error_decomposition(blocks, O.MODE_CEIL)
+    assert np.all(d["e_dz"] * d["e_scale"] == 0.0)
+    assert np.all(d["e_dz"] * d["e_grid"] == 0.0)
+    assert np.sum(d["e_dz"] * d["e_scale"]) == 0.0
+    assert np.sum(d["e_dz"] * d["e_grid"]) == 0.0
+    assert np.array_equal(d["e"], d["e_scale"] + d["e_dz"] + d["e_grid"]) or \
+        np.allclose(d["e"], d["e_scale"] + d["e_dz"] + d["e_grid"], rtol=0, atol=1e-12)
+    # deadzone edges are really exercised
+    assert d["deadzone"][:, 1].any() and (~d["deadzone"][:, 1]).any()
+
+
+def test_orthogonality_random_blocks_and_mse_identity():
+    rng = np.random.default_rng(9)
+    a = rng.standard_t(3, size=(100_000, 32)) * rng.lognormal(0, 1, size=(100_000, 1))
+    blocks = O.bf16_to_f32(synthetic.f64_to_bf16_bits(a))
+    d = O.error_decomposition(blocks, O.MODE_CEIL)
+    assert np.sum(d["e_dz"] * d["e_scale"]) == 0.0
+    assert np.sum(d["e_dz"] * d["e_grid"]) == 0.0
+    es, ez, eg, e = d["e_scale"], d["e_dz"], d["e_grid"], d["e"]
+    lhs = np.sum(e * e)
+    rhs = np.sum(es * es) + np.sum(ez * ez) + np.sum(eg * eg) + 2 * np.sum(es * eg)
+    assert abs(lhs - rhs) <= 1e-12 * lhs
+    # cross term is anti-correlated under the ceiling scale ([P3] Property 1)
+    cos = np.sum(es * eg) / np.sqrt(np.sum(es * es) * np.sum(eg * eg))
+    assert cos < 0
+
+
+def test_floor_mode_breaks_the_lemma_premise():
+    """Under the OCP floor rule s_b can be below s* (m_b = 7: s_b = 1 < 7/6),
+    so <e_DZ, e_scale> need not vanish; the disjoint-support term still does.
+    Hand-worked: block {7, 0.27, 0...}: floor E = 0, 0.27 -> code 1 (0.5);
+    ideal s* = 7/6, 0.27 / s* = 0.2314 < 0.25 -> 0 (deadzone: 24*0.27 < 7)."""
+    blk = np.zeros((1, 32), dtype=np.float32)
+    blk[0, 0] = 7.0
+    blk[0, 1] = np.float32(0.27)
+    d = O.error_decomposition(blk, O.MODE_OCP_FLOOR)
+    assert d["E"][0] == 0
+    assert d["Q"][0, 0] == 6.0 and d["Q"][0, 1] == 0.5
+    assert d["deadzone"][0, 1] and d["Q_star"][0, 1] == 0.0
+    x1 = float(np.float32(0.27))
+    assert np.sum(d["e_dz"] * d["e_scale"]) == pytest.approx(-x1 * 0.5, rel=1e-12)
+    assert np.sum(d["e_dz"] * d["e_grid"]) == 0.0
+    dc = O.error_decomposition(blk, O.MODE_CEIL)
+    assert dc["E"][0] == 1 and dc["Q"][0, 1] == 0.0
+
+
+# ------------------------------------------------------- hand-worked blocks
+def test_hand_worked_blocks():
+    """Blocks whose encodings follow from the definitions by hand."""
+    # max 7 = 1.75 * 2^2: floor E = 0 (7 -> 6 saturates); ceil needs
+    # 6 * 2^E >= 7 -> E = 1 (7/2 = 3.5 is a tie -> 4, code 6).
+    blk = np.zeros((1, 32), dtype=np.float32)
+    blk[0, :4] = [7.0, -1.0, 0.25, 3.0]
+    src = synthetic.f64_to_bf16_bits(blk)
+    nib, sc = O.quantize(src, O.AXIS_ROW, 0, O.MODE_OCP_FLOOR)
+    assert sc[0, 0] == 127
+    assert nib[0, 0] == (7 | (8 | 2) << 4) and nib[0, 1] == (0 | 5 << 4)
+    nib, sc = O.quantize(src, O.AXIS_ROW, 0, O.MODE_CEIL)
+    assert sc[0, 0] == 128
+    # 7/2 = 3.5 -> 4 (code 6); -1/2 -> -0.5 (code 9); 0.125 -> 0; 1.5 -> code 3
+    assert nib[0, 0] == (6 | 9 << 4) and nib[0, 1] == (0 | 3 << 4)
+    # all-zero block (with a negative zero): scale byte 0, codes keep the sign
+    z = np.zeros((1, 32), dtype=np.uint16)
+    z[0, 1] = 0x8000
+    nib, sc = O.quantize(z, O.AXIS_ROW, 0, O.MODE_CEIL)
+    assert sc[0, 0] == 0 and nib[0, 0] == 0x80 and np.all(nib[0, 1:] == 0)
+    # a non-finite value poisons its block: scale 0xFF, zero nibbles
+    z[0, 5] = 0x7F80
+    nib, sc = O.quantize(z, O.AXIS_ROW, 0, O.MODE_CEIL)
+    assert sc[0, 0] == 255 and np.all(nib == 0)
+    # H16 of a constant group: all energy moves to element 0 of the group
+    c = np.full((1, 32), 2.0)
+    y = O.hadamard_rotate(c.astype(np.float32), 16)
+    assert y[0, 0] == 8.0 and y[0, 16] == 8.0 and np.count_nonzero(y) == 2
+
+
+# -------------------------------------------------------------- GEMM oracle
+def test_gemm_ref_against_exact_sum():
+    """fp64 product of dequantized operands vs exact rational sums."""
+    rng = np.random.default_rng(21)
+    A = synthetic.f64_to_bf16_bits(rng.normal(size=(5, 64)))
+    B = synthetic.f64_to_bf16_bits(rng.normal(size=(3, 64)) * 30)
+    qa = O.quantize(A, O.AXIS_ROW, 16, O.MODE_OCP_FLOOR)
+    qb = O.quantize(B, O.AXIS_ROW, 16, O.MODE_OCP_FLOOR)
+    da, db = O.dequantize(*qa), O.dequantize(*qb)
+    C, S = O.gemm_ref(da, db)
+    for i in range(5):
+        for j in range(3):
+            exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(da[i], db[j]))
+            sabs = sum(abs(Fraction(float(a)) * Fraction(float(b))) for a, b in zip(da[i], db[j]))
+            assert abs(Fraction(C[i, j]) - exact) <= Fraction(64) * Fraction(2) ** -52 * sabs
+            assert abs(Fraction(S[i, j]) - sabs) <= Fraction(64) * Fraction(2) ** -52 * sabs
+    # orientation: C[i, j] pairs A's row i with B's row j
+    assert C.shape == (5, 3)
+
+
+def test_product_operand_orientation():
+    """dgrad quantizes W column-wise (so B is W^T, [K][N]); wgrad quantizes
+    both operands column-wise (A = dY^T, B = X^T). Dequantized products of
+    unrotated small-integer operands reproduce the plain products exactly
+    when every block is exactly representable."""
+    rng = np.random.default_rng(4)
+    T, N, K = 64, 32, 96
+    # values in {0, +-1, +-2, +-4} * 2^k fit the E2M1 grid after scaling
+    def grid_ints(shape):
+        return rng.choice([0.0, 1.0, -1.0, 2.0, -2.0, 4.0, -4.0], size=shape)
+    P_f = grid_ints((T, N))
+    Q_f = grid_ints((N, K))
+    X_f = grid_ints((T, K))
+    for op, P, Q, want in (
+        ("dgrad", P_f, Q_f, P_f @ Q_f),
+        ("wgrad", P_f, X_f, P_f.T @ X_f),
+        ("fprop", X_f, grid_ints((N, K)), None),
+    ):
+        Pb, Qb = synthetic.f64_to_bf16_bits(P), synthetic.f64_to_bf16_bits(Q)
+        (an, asc), (bn, bsc) = O.product_operands(op, Pb, Qb, 0, O.MODE_CEIL)
+        C, _ = O.gemm_ref(O.dequantize(an, asc), O.dequantize(bn, bsc))
+        if want is None:
+            want = P @ Q.T
+        assert np.array_equal(C, want), op
