@@ -1,0 +1,157 @@
+/*
+ * mxfp4.h -- C ABI of the MI355X (gfx950) H16 + MXFP4 quantize + MXFP4 GEMM
+ * library (libmxfp4.so).
+ *
+ * Pages cited (by title and section):
+ *  [P1] "Pretraining Large Language Models with MXFP4 on Native FP4 Hardware"
+ *       (arXiv:2605.09825, summary page): quick-read block and section A.1
+ *       (MX block reconstruction x_rec = 2^E * Q_FP4(x / 2^E), shared exponent
+ *       taken from the block maximum, round to the nearest FP4 value);
+ *       section A.2 (deterministic tiled 16x16 Hadamard injected before each
+ *       MXFP4 GEMM; FP8 GEMMs replaced per product Fprop/Dgrad/Wgrad);
+ *       sections C.1-C.3 (cancellation H H^T = I in the three products);
+ *       section D (1x32 row-wise, 32x1 column-wise, 32x32 2D block scales).
+ *  [P3] "Decomposing MXFP4 quantization error" blog (arXiv:2605.20402),
+ *       pain-point section (OCP MX: 32 elements, E8M0 scale 2^n, E2M1 grid
+ *       {0, +-0.5, +-1, +-1.5, +-2, +-3, +-4, +-6}); core-insight section
+ *       (ceiling-rounded E8M0 scale of s* = max|x| / 6); note that native
+ *       MXFP4 GEMMs accumulate in FP32.
+ *
+ * Conventions shared by every entry point
+ *  - All data pointers are DEVICE pointers owned by the caller. The library
+ *    never allocates, frees or synchronizes; every call only enqueues
+ *    kernels on `stream` (0 = the null stream) and returns.
+ *  - bf16 inputs are row-major with a dense row pitch.
+ *  - Packed MXFP4 operand ("nibbles + E8M0 bytes"): nibble byte j of a row
+ *    holds element 2j in bits 0-3 and element 2j+1 in bits 4-7; an element
+ *    code is sign << 3 | magnitude code (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6
+ *    for codes 0..7). One E8M0 byte (value 2^(byte - 127), 0xFF = NaN) per
+ *    block of 32 elements along the row.
+ *  - Every check runs on the host before any HIP call; a failed check
+ *    returns its status and launches nothing. After launching, a pending
+ *    HIP launch error is returned as MXFP4_ERR_HIP.
+ *  - Pointers handed to vector loads/stores must be 16-byte aligned
+ *    (bf16 sources, nibble outputs, GEMM operands); scale arrays and C need
+ *    no alignment beyond their element size.
+ *  - Calls are thread-safe (no global state); concurrent calls on one stream
+ *    run in stream order.
+ */
+#ifndef MXFP4_H_
+#define MXFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MXFP4_OK = 0,
+  MXFP4_ERR_NULL = 1,      /* a required pointer is NULL                       */
+  MXFP4_ERR_SHAPE = 2,     /* a size is negative, zero where not allowed, or not
+                              a multiple of the block / Hadamard size           */
+  MXFP4_ERR_MODE = 3,      /* axis, hadamard, scale_mode or out_dtype invalid  */
+  MXFP4_ERR_WORKSPACE = 4, /* ws_bytes below mxfp4_workspace_bytes()           */
+  MXFP4_ERR_HIP = 5,       /* the HIP runtime reported an error on launch      */
+  MXFP4_ERR_ALIGN = 6      /* a vector-accessed pointer is not 16-byte aligned */
+} mxfp4_status;
+
+typedef enum {
+  MXFP4_AXIS_ROW = 0,  /* 1x32 blocks along cols ([P1] D, row-wise)            */
+  MXFP4_AXIS_COL = 1,  /* 32x1 blocks down rows, transposed output ([P1] D)    */
+  MXFP4_AXIS_2D32 = 2  /* one scale per 32x32 tile ([P1] D, 2D)                */
+} mxfp4_axis;
+
+typedef enum {
+  MXFP4_SCALE_OCP_FLOOR = 0, /* E = floor(log2 amax) - 2 ([P1] A.1 with the OCP
+                                MX offset of E2M1's largest exponent)          */
+  MXFP4_SCALE_CEIL = 1       /* smallest E with 6 * 2^E >= amax ([P3])         */
+} mxfp4_scale_mode;
+
+typedef enum { MXFP4_OUT_F32 = 0, MXFP4_OUT_BF16 = 1 } mxfp4_out;
+
+typedef enum { MXFP4_OP_FPROP = 0, MXFP4_OP_DGRAD = 1, MXFP4_OP_WGRAD = 2 } mxfp4_op;
+
+/*
+ * mxfp4_quantize -- rotate then MXFP4-quantize a bf16 matrix src[rows][cols].
+ * ([P1] A.1 and D; rotation [P1] A.2; grid and scale rules [P3].)
+ *
+ * hadamard: 0 (no rotation), 16 or 32. Each aligned group of `hadamard`
+ *   elements along the rotated axis becomes x * H, H the Sylvester matrix
+ *   scaled by 1/4 (H16) or RN_fp32(2^-2.5) (H32), evaluated as the fp32
+ *   butterfly with stages 1, 2, 4, 8 (, 16) and one final multiply.
+ * Per block of 32 rotated values: amax m_b; E8M0 exponent E by scale_mode
+ *   (zero block: E = -127; clamp to [-127, 127]); element codes are the
+ *   nearest E2M1 value of y / 2^E, ties to the even code, saturating at 6,
+ *   sign bit kept. A block holding a non-finite rotated value gets scale
+ *   byte 0xFF and all-zero nibbles.
+ *
+ * axis = MXFP4_AXIS_ROW: rotate and block along cols. cols % 32 == 0.
+ *   out_nibbles [rows][cols/2], out_e8m0 [rows][cols/32].
+ * axis = MXFP4_AXIS_COL: rotate and block down rows; the output is the
+ *   transposed operand (K-contiguous for the GEMM). rows % 32 == 0.
+ *   out_nibbles [cols][rows/2], out_e8m0 [cols][rows/32].
+ * axis = MXFP4_AXIS_2D32: rotate along cols, one scale per 32x32 tile.
+ *   rows % 32 == 0, cols % 32 == 0.
+ *   out_nibbles [rows][cols/2], out_e8m0 [rows/32][cols/32].
+ * rows == 0 or cols == 0 is a valid empty call (nothing is launched).
+ * Outputs are fully overwritten. Deterministic: identical inputs give
+ * identical bytes.
+ */
+int mxfp4_quantize(const void* src_bf16, int64_t rows, int64_t cols, int axis,
+                   int hadamard, int scale_mode, void* out_nibbles, void* out_e8m0,
+                   hipStream_t stream);
+
+/*
+ * mxfp4_gemm -- C[M][N] = sum_k deqA[m][k] * deqB[n][k] on gfx950's
+ * block-scaled FP4 MFMA with FP32 accumulation ([P1] A.2; [P3]).
+ *
+ * A: Aq [M][K/2] nibbles, As [M][K/32] E8M0 bytes.
+ * B: Bq [N][K/2] nibbles, Bs [N][K/32] E8M0 bytes (both K-contiguous).
+ * C: row-major [M][N], fp32 (out_dtype 0) or bf16 (1, round to nearest
+ *    even from the fp32 accumulator). C is overwritten, not accumulated.
+ * M >= 1, N >= 1, K >= 32, K % 32 == 0. Any M and N (edge tiles are
+ * predicated).
+ */
+int mxfp4_gemm(const void* Aq, const void* As, const void* Bq, const void* Bs,
+               int64_t M, int64_t N, int64_t K, void* C, int out_dtype,
+               hipStream_t stream);
+
+/*
+ * Fused linear-layer products ([P1] C.1, C.2, C.3). Each quantizes both
+ * operands with the same `hadamard` and `scale_mode`, rotating along the
+ * product's reduction axis, into the caller's workspace `ws` (ws_bytes >=
+ * mxfp4_workspace_bytes(op, T, N, K), 256-byte aligned), then runs
+ * mxfp4_gemm. Three launches on `stream`. Shapes follow Y = X W^T with
+ * X [T][K], W [N][K], Y [T][N]:
+ *
+ * mxfp4_fprop: Y[T][N]  = X[T][K] W[N][K]^T. X, W quantized row-wise along
+ *              K. K % 32 == 0.
+ * mxfp4_dgrad: dX[T][K] = dY[T][N] W[N][K]. dY row-wise along N, W
+ *              column-wise along N (transposed to [K][N]). N % 32 == 0.
+ * mxfp4_wgrad: dW[N][K] = dY[T][N]^T X[T][K]. dY and X column-wise along
+ *              the token axis T. T % 32 == 0.
+ */
+int mxfp4_fprop(const void* X, const void* W, int64_t T, int64_t N, int64_t K,
+                int hadamard, int scale_mode, void* ws, size_t ws_bytes, void* Y,
+                int out_dtype, hipStream_t stream);
+int mxfp4_dgrad(const void* dY, const void* W, int64_t T, int64_t N, int64_t K,
+                int hadamard, int scale_mode, void* ws, size_t ws_bytes, void* dX,
+                int out_dtype, hipStream_t stream);
+int mxfp4_wgrad(const void* dY, const void* X, int64_t T, int64_t N, int64_t K,
+                int hadamard, int scale_mode, void* ws, size_t ws_bytes, void* dW,
+                int out_dtype, hipStream_t stream);
+
+/* Workspace bytes of a fused product (op: mxfp4_op): both packed operands,
+ * each piece rounded up to 256 bytes. Returns 0 for invalid arguments. */
+size_t mxfp4_workspace_bytes(int op, int64_t T, int64_t N, int64_t K);
+
+/* Static text of a status code ("MXFP4_OK", ...); never NULL. */
+const char* mxfp4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXFP4_H_ */

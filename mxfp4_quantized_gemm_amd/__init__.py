@@ -1,0 +1,227 @@
+"""Python binding of libmxfp4 (MI355X / gfx950 H16 + MXFP4 quantize + GEMM).
+
+Thin ctypes marshalling over the C ABI declared in ``include/mxfp4.h``: the
+functions below carry the C names, take torch tensors (device memory) and
+the current HIP stream, check shapes and dtypes, and call the library.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback. If ``libmxfp4.so`` has not been built, every call raises.
+
+Layouts (see the header): bf16 sources are row-major; a packed MXFP4
+operand is ``nibbles`` (uint8, two E2M1 codes per byte, element 2j in the
+low nibble) plus ``e8m0`` (uint8, one scale byte per 32-element block).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+AXIS_ROW, AXIS_COL, AXIS_2D32 = 0, 1, 2
+SCALE_OCP_FLOOR, SCALE_CEIL = 0, 1
+OUT_F32, OUT_BF16 = 0, 1
+OP_FPROP, OP_DGRAD, OP_WGRAD = 0, 1, 2
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp4.so")
+
+EXPORTS = (
+    "mxfp4_quantize", "mxfp4_gemm", "mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad",
+    "mxfp4_workspace_bytes", "mxfp4_status_string",
+)
+
+_LIB = None
+
+
+class MXFP4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmxfp4.so (once) and declare the C signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m mxfp4_quantized_gemm_amd.build`")
+    lib = ctypes.CDLL(path)
+    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.mxfp4_quantize.argtypes = [p, i64, i64, i32, i32, i32, p, p, p]
+    lib.mxfp4_quantize.restype = i32
+    lib.mxfp4_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
+    lib.mxfp4_gemm.restype = i32
+    for name in ("mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad"):
+        fn = getattr(lib, name)
+        fn.argtypes = [p, p, i64, i64, i64, i32, i32, p, sz, p, i32, p]
+        fn.restype = i32
+    lib.mxfp4_workspace_bytes.argtypes = [i32, i64, i64, i64]
+    lib.mxfp4_workspace_bytes.restype = sz
+    lib.mxfp4_status_string.argtypes = [i32]
+    lib.mxfp4_status_string.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().mxfp4_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise MXFP4Error(status, where)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, dtype, numel, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live in GPU memory")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+
+
+# ----------------------------------------------------------------- C calls
+def mxfp4_quantize(src, rows, cols, axis, hadamard, scale_mode, out_nibbles, out_e8m0,
+                   stream=None):
+    """Rotate + quantize ``src`` (bf16 [rows][cols]) into caller buffers."""
+    import torch
+    _need(src, torch.bfloat16, rows * cols, "src")
+    nib, nsc = packed_sizes(rows, cols, axis)
+    _need(out_nibbles, torch.uint8, nib, "out_nibbles")
+    _need(out_e8m0, torch.uint8, nsc, "out_e8m0")
+    _check(load_library().mxfp4_quantize(_ptr(src), rows, cols, axis, hadamard, scale_mode,
+                                         _ptr(out_nibbles), _ptr(out_e8m0), _stream(stream)),
+           "mxfp4_quantize")
+
+
+def mxfp4_gemm(Aq, As, Bq, Bs, M, N, K, C, out_dtype=OUT_F32, stream=None):
+    """C[M][N] = deq(A) deq(B)^T from packed K-contiguous operands."""
+    import torch
+    _need(Aq, torch.uint8, M * K // 2, "Aq")
+    _need(As, torch.uint8, M * K // 32, "As")
+    _need(Bq, torch.uint8, N * K // 2, "Bq")
+    _need(Bs, torch.uint8, N * K // 32, "Bs")
+    _need(C, torch.float32 if out_dtype == OUT_F32 else torch.bfloat16, M * N, "C")
+    _check(load_library().mxfp4_gemm(_ptr(Aq), _ptr(As), _ptr(Bq), _ptr(Bs), M, N, K, _ptr(C),
+                                     out_dtype, _stream(stream)), "mxfp4_gemm")
+
+
+def _fused(name, op, P, Q, T, N, K, hadamard, scale_mode, ws, out, out_dtype, stream, pshape,
+           qshape, oshape):
+    import torch
+    _need(P, torch.bfloat16, pshape[0] * pshape[1], "first operand")
+    _need(Q, torch.bfloat16, qshape[0] * qshape[1], "second operand")
+    _need(out, torch.float32 if out_dtype == OUT_F32 else torch.bfloat16,
+          oshape[0] * oshape[1], "output")
+    need = mxfp4_workspace_bytes(op, T, N, K)
+    _need(ws, torch.uint8, need, "workspace")
+    _check(getattr(load_library(), name)(_ptr(P), _ptr(Q), T, N, K, hadamard, scale_mode,
+                                         _ptr(ws), ws.numel(), _ptr(out), out_dtype,
+                                         _stream(stream)), name)
+
+
+def mxfp4_fprop(X, W, T, N, K, hadamard, scale_mode, ws, Y, out_dtype=OUT_F32, stream=None):
+    """Y[T][N] = X[T][K] W[N][K]^T (both operands rotated along K)."""
+    _fused("mxfp4_fprop", OP_FPROP, X, W, T, N, K, hadamard, scale_mode, ws, Y, out_dtype,
+           stream, (T, K), (N, K), (T, N))
+
+
+def mxfp4_dgrad(dY, W, T, N, K, hadamard, scale_mode, ws, dX, out_dtype=OUT_F32, stream=None):
+    """dX[T][K] = dY[T][N] W[N][K] (both rotated along N)."""
+    _fused("mxfp4_dgrad", OP_DGRAD, dY, W, T, N, K, hadamard, scale_mode, ws, dX, out_dtype,
+           stream, (T, N), (N, K), (T, K))
+
+
+def mxfp4_wgrad(dY, X, T, N, K, hadamard, scale_mode, ws, dW, out_dtype=OUT_F32, stream=None):
+    """dW[N][K] = dY[T][N]^T X[T][K] (both rotated along T)."""
+    _fused("mxfp4_wgrad", OP_WGRAD, dY, X, T, N, K, hadamard, scale_mode, ws, dW, out_dtype,
+           stream, (T, N), (T, K), (N, K))
+
+
+def mxfp4_workspace_bytes(op, T, N, K) -> int:
+    return int(load_library().mxfp4_workspace_bytes(op, T, N, K))
+
+
+def mxfp4_status_string(status: int) -> str:
+    return status_string(status)
+
+
+# ------------------------------------------------------ allocating helpers
+def packed_sizes(rows, cols, axis):
+    """(nibble bytes, scale bytes) of ``mxfp4_quantize``'s outputs."""
+    if axis == AXIS_2D32:
+        return rows * cols // 2, (rows // 32) * (cols // 32)
+    return rows * cols // 2, rows * cols // 32
+
+
+def packed_shapes(rows, cols, axis):
+    """Shapes of (nibbles, e8m0) for a bf16 [rows][cols] source."""
+    if axis == AXIS_COL:
+        return (cols, rows // 2), (cols, rows // 32)
+    if axis == AXIS_2D32:
+        return (rows, cols // 2), (rows // 32, cols // 32)
+    return (rows, cols // 2), (rows, cols // 32)
+
+
+def quantize(src, axis=AXIS_ROW, hadamard=16, scale_mode=SCALE_OCP_FLOOR, stream=None):
+    """Allocate outputs and quantize; returns (nibbles, e8m0) uint8 tensors."""
+    import torch
+    rows, cols = src.shape
+    ns, ss = packed_shapes(rows, cols, axis)
+    nib = torch.empty(ns, dtype=torch.uint8, device=src.device)
+    sc = torch.empty(ss, dtype=torch.uint8, device=src.device)
+    mxfp4_quantize(src, rows, cols, axis, hadamard, scale_mode, nib, sc, stream)
+    return nib, sc
+
+
+def gemm(Aq, As, Bq, Bs, out_dtype=OUT_F32, stream=None):
+    """Allocate C and run the MXFP4 GEMM on packed operands."""
+    import torch
+    M, kh = Aq.shape
+    N = Bq.shape[0]
+    C = torch.empty((M, N), dtype=torch.float32 if out_dtype == OUT_F32 else torch.bfloat16,
+                    device=Aq.device)
+    mxfp4_gemm(Aq, As, Bq, Bs, M, N, 2 * kh, C, out_dtype, stream)
+    return C
+
+
+def linear(op, P, Q, hadamard=16, scale_mode=SCALE_OCP_FLOOR, out_dtype=OUT_F32, ws=None,
+           stream=None):
+    """One fused product ('fprop', 'dgrad' or 'wgrad'); allocates the output."""
+    import torch
+    if op == "fprop":
+        T, K = P.shape
+        N = Q.shape[0]
+        oshape, fn, code = (T, N), mxfp4_fprop, OP_FPROP
+    elif op == "dgrad":
+        T, N = P.shape
+        K = Q.shape[1]
+        oshape, fn, code = (T, K), mxfp4_dgrad, OP_DGRAD
+    elif op == "wgrad":
+        T, N = P.shape
+        K = Q.shape[1]
+        oshape, fn, code = (N, K), mxfp4_wgrad, OP_WGRAD
+    else:
+        raise ValueError(op)
+    if ws is None:
+        ws = torch.empty(mxfp4_workspace_bytes(code, T, N, K), dtype=torch.uint8, device=P.device)
+    out = torch.empty(oshape, dtype=torch.float32 if out_dtype == OUT_F32 else torch.bfloat16,
+                      device=P.device)
+    fn(P, Q, T, N, K, hadamard, scale_mode, ws, out, out_dtype, stream)
+    return out

@@ -1,0 +1,19 @@
+// Internal launch interface between the host API (api.cpp) and the gfx950
+// kernels (quant.hip, gemm.hip). Arguments are validated by the caller.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace mx {
+
+// Rotate + quantize (see mxfp4_quantize in include/mxfp4.h for semantics).
+hipError_t launch_quantize(const void* src, int64_t rows, int64_t cols, int axis,
+                           int hadamard, int scale_mode, void* nib, void* sc,
+                           hipStream_t stream);
+
+// Block-scaled MXFP4 GEMM, C[M][N] = A[M][K] B[N][K]^T.
+hipError_t launch_gemm(const void* Aq, const void* As, const void* Bq, const void* Bs,
+                       int64_t M, int64_t N, int64_t K, void* C, int out_dtype,
+                       hipStream_t stream);
+
+}  // namespace mx

@@ -1,0 +1,310 @@
+// Rotate + MXFP4-quantize kernels for gfx950 (MI355X).
+//
+// Pages cited: [P1] "Pretraining Large Language Models with MXFP4 on Native
+// FP4 Hardware" (arXiv:2605.09825 summary), section A.1 (MX reconstruction,
+// shared exponent from the block maximum, nearest FP4 value), A.2
+// (deterministic tiled Hadamard before the GEMM), D (1x32 / 32x1 / 32x32
+// scale layouts); [P3] "Decomposing MXFP4 quantization error" blog
+// (arXiv:2605.20402), pain-point and core-insight sections (32-element OCP
+// MX block, E8M0 scale, E2M1 grid, ceiling-rounded scale of max|x| / 6).
+//
+// Every kernel is HBM-bound: it reads 2 B/element of bf16 and writes
+// 0.5 B/element of packed E2M1 plus one E8M0 byte per block. Per element the
+// ALU work is the widening shift, the fp32 butterfly (log2 h add/sub), one
+// multiply by the Hadamard normalisation, an integer max for the block amax
+// and half of one v_cvt_scalef32_pk_fp4_f32 (gfx950's scaled FP4 convert,
+// which rounds x / 2^E to nearest-even E2M1 and saturates at 6).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace mx {
+namespace {
+
+constexpr int kOcpFloor = 0;
+constexpr int kCeil = 1;
+
+__device__ __forceinline__ float bf16lo(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t d) { return __uint_as_float(d & 0xffff0000u); }
+
+// fp32 Walsh-Hadamard butterfly on every aligned group of H values of v[32]:
+// for s = 1, 2, 4, ... H/2 each pair (i, i+s) with (i & s) == 0 becomes
+// (a + b, a - b); then one multiply by 1/4 (H16) or RN(2^-2.5) (H32).
+// The order of operations is part of the definition; every add is one
+// fp32 round-to-nearest-even step (no reassociation, no contraction).
+template <int H>
+__device__ __forceinline__ void hadamard32(float (&v)[32]) {
+  if constexpr (H != 0) {
+#pragma unroll
+    for (int s = 1; s < H; s <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if ((i & s) == 0) {
+          const float a = v[i], b = v[i + s];
+          v[i] = a + b;
+          v[i + s] = a - b;
+        }
+      }
+    }
+    const float c = (H == 16) ? 0.25f : __uint_as_float(0x3E3504F3u);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] *= c;
+  }
+}
+
+// Largest |v| as fp32 bits. Integer max over the sign-cleared patterns is
+// exact and orders NaN (> 0x7f800000) above +Inf above every finite value.
+__device__ __forceinline__ uint32_t amax_bits32(const float (&v)[32]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(v[i]) & 0x7fffffffu);
+  return m;
+}
+
+// E8M0 byte (E + 127) of a block whose amax has fp32 bits `a`; 0xFF when the
+// block holds a non-finite value. amax = m * 2^e, m in [1, 2):
+// ocp_floor E = e - 2; ceil E = e - 2 + (m > 1.5). A zero or subnormal amax
+// (e <= -127) lands below the clamp, so E = -127. E never exceeds 126.
+template <int MODE>
+__device__ __forceinline__ uint32_t e8m0_byte(uint32_t a) {
+  if (a >= 0x7f800000u) return 255u;
+  const int be = (int)(a >> 23);
+  int E = be - 129;
+  if (MODE == kCeil && (a & 0x7fffffu) > 0x400000u) E += 1;
+  if (be == 0) E = -127;
+  E = max(E, -127);
+  return (uint32_t)(E + 127);
+}
+
+// 2^(byte - 127) as fp32 (byte 0 is the subnormal 2^-127).
+__device__ __forceinline__ float scale_of_byte(uint32_t s) {
+  return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);
+}
+
+// 32 rotated values -> 16 bytes of packed E2M1 (element 2j in the low
+// nibble of byte j). The convert returns code(x / scale) with RNE ties
+// and saturation; its op_sel picks the destination byte.
+__device__ __forceinline__ uint4 encode32(const float (&v)[32], float scale) {
+  uint32_t w[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * d + 0], v[8 * d + 1], scale, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * d + 2], v[8 * d + 3], scale, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * d + 4], v[8 * d + 5], scale, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[8 * d + 6], v[8 * d + 7], scale, 3);
+    w[d] = r;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ void unpack64B(const uint4 (&q)[4], float (&v)[32]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t d[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[8 * j + 2 * k] = bf16lo(d[k]);
+      v[8 * j + 2 * k + 1] = bf16hi(d[k]);
+    }
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ void encode_block(const float (&v)[32], uint4& nib, uint32_t& s) {
+  s = e8m0_byte<MODE>(amax_bits32(v));
+  nib = (s == 255u) ? make_uint4(0, 0, 0, 0) : encode32(v, scale_of_byte(s));
+}
+
+// ---------------------------------------------------------------- row (1x32)
+// One thread per 32-element block of a row-major matrix whose rows are a
+// multiple of 32 long, so block b covers elements [32b, 32b + 32) of the
+// flat array and owns nibble bytes [16b, 16b + 16) and scale byte b.
+template <int H, int MODE>
+__global__ __launch_bounds__(256) void quant_row_kernel(const uint4* __restrict__ src,
+                                                        int64_t nblocks,
+                                                        uint4* __restrict__ nib,
+                                                        uint8_t* __restrict__ sc) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  uint4 q[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) q[j] = src[b * 4 + j];
+  float v[32];
+  unpack64B(q, v);
+  hadamard32<H>(v);
+  uint4 out;
+  uint32_t s;
+  encode_block<MODE>(v, out, s);
+  nib[b] = out;
+  sc[b] = (uint8_t)s;
+}
+
+// ----------------------------------------------------------- 2D (32x32 tile)
+// Work-group = 32 rows x 8 column blocks (256 threads, one 1x32 block each);
+// thread t: column block t & 7, row t >> 3. The tile amax is reduced across
+// the 32 rows with lane shuffles (xor 8, 16, 32) and then across the four
+// waves through LDS. Grid is flat: tile-row major over (rows/32, ceil(ncb/8)).
+template <int H, int MODE>
+__global__ __launch_bounds__(256) void quant_2d_kernel(const uint16_t* __restrict__ src,
+                                                       int64_t rows, int64_t cols,
+                                                       uint8_t* __restrict__ nib,
+                                                       uint8_t* __restrict__ sc) {
+  __shared__ uint32_t red[4][8];
+  const int t = threadIdx.x;
+  const int cbl = t & 7, r = t >> 3;
+  const int64_t ncb = cols / 32;
+  const int64_t ngrp = (ncb + 7) / 8;
+  const int64_t tile_row = (int64_t)blockIdx.x / ngrp;
+  const int64_t cb = ((int64_t)blockIdx.x % ngrp) * 8 + cbl;
+  const int64_t row = tile_row * 32 + r;
+  const bool active = cb < ncb;
+  float v[32];
+  if (active) {
+    const uint4* p = reinterpret_cast<const uint4*>(src + row * cols + cb * 32);
+    uint4 q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) q[j] = p[j];
+    unpack64B(q, v);
+    hadamard32<H>(v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = 0.f;
+  }
+  uint32_t am = amax_bits32(v);
+  am = max(am, (uint32_t)__shfl_xor((int)am, 8));
+  am = max(am, (uint32_t)__shfl_xor((int)am, 16));
+  am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+  const int wave = t >> 6;
+  if ((t & 63) < 8) red[wave][cbl] = am;
+  __syncthreads();
+  am = max(max(red[0][cbl], red[1][cbl]), max(red[2][cbl], red[3][cbl]));
+  if (!active) return;
+  const uint32_t s = e8m0_byte<MODE>(am);
+  const uint4 out = (s == 255u) ? make_uint4(0, 0, 0, 0) : encode32(v, scale_of_byte(s));
+  reinterpret_cast<uint4*>(nib + row * (cols / 2))[cb] = out;
+  if (r == 0) sc[tile_row * ncb + cb] = (uint8_t)s;
+}
+
+// ------------------------------------------------------ column (32x1, transposed)
+// Vector path (cols % 8 == 0). Work-group = 4 waves; the flat grid walks
+// (row group of 128, column group of 512) with the column group fastest.
+// Lane l of wave w owns columns [c0, c0 + 8), c0 = group*512 + 8l, for the
+// 32-row band 4*rowgroup + w: it loads the band with 32 coalesced 16-byte
+// loads (a wave reads 1 KB contiguous per row), so each of its 8 columns'
+// 32x1 block sits in its own registers and the rotation down the rows needs
+// no data exchange. Output row c of the transposed operand receives the
+// band's 16 nibble bytes at offset 16*band and its scale byte at `band`.
+template <int H, int MODE>
+__global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restrict__ src,
+                                                        int64_t rows, int64_t cols,
+                                                        uint8_t* __restrict__ nib,
+                                                        uint8_t* __restrict__ sc) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t ncg = (cols + 511) / 512;
+  const int64_t cg = (int64_t)blockIdx.x % ncg;
+  const int64_t rg = (int64_t)blockIdx.x / ncg;
+  const int64_t band = rg * 4 + wave;
+  const int64_t c0 = cg * 512 + (int64_t)lane * 8;
+  if (band * 32 >= rows || c0 >= cols) return;
+  const uint16_t* p = src + band * 32 * cols + c0;
+  uint4 raw[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) raw[r] = *reinterpret_cast<const uint4*>(p + r * cols);
+  const int64_t nib_pitch = rows / 2, sc_pitch = rows / 32;
+#pragma unroll
+  for (int pr = 0; pr < 4; ++pr) {
+    float a[32], b[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      const uint32_t d = pr == 0 ? raw[r].x : pr == 1 ? raw[r].y : pr == 2 ? raw[r].z : raw[r].w;
+      a[r] = bf16lo(d);
+      b[r] = bf16hi(d);
+    }
+    hadamard32<H>(a);
+    hadamard32<H>(b);
+    uint4 na, nb;
+    uint32_t sa, sb;
+    encode_block<MODE>(a, na, sa);
+    encode_block<MODE>(b, nb, sb);
+    const int64_t ca = c0 + 2 * pr, cb = ca + 1;
+    *reinterpret_cast<uint4*>(nib + ca * nib_pitch + band * 16) = na;
+    *reinterpret_cast<uint4*>(nib + cb * nib_pitch + band * 16) = nb;
+    sc[ca * sc_pitch + band] = (uint8_t)sa;
+    sc[cb * sc_pitch + band] = (uint8_t)sb;
+  }
+}
+
+// Scalar path for any cols: one thread per (column, 32-row band); loads are
+// 2-byte, coalesced across the threads of a row.
+template <int H, int MODE>
+__global__ __launch_bounds__(256) void quant_col_scalar_kernel(const uint16_t* __restrict__ src,
+                                                               int64_t rows, int64_t cols,
+                                                               uint8_t* __restrict__ nib,
+                                                               uint8_t* __restrict__ sc) {
+  const int64_t ncg = (cols + 255) / 256;
+  const int64_t c = ((int64_t)blockIdx.x % ncg) * 256 + threadIdx.x;
+  const int64_t band = (int64_t)blockIdx.x / ncg;
+  if (c >= cols || band * 32 >= rows) return;
+  float v[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) v[r] = __uint_as_float((uint32_t)src[(band * 32 + r) * cols + c] << 16);
+  hadamard32<H>(v);
+  uint4 out;
+  uint32_t s;
+  encode_block<MODE>(v, out, s);
+  *reinterpret_cast<uint4*>(nib + c * (rows / 2) + band * 16) = out;
+  sc[c * (rows / 32) + band] = (uint8_t)s;
+}
+
+template <int H, int MODE>
+hipError_t dispatch_axis(const void* src, int64_t rows, int64_t cols, int axis, void* nib,
+                         void* sc, hipStream_t st) {
+  const dim3 blk(256);
+  if (axis == 0) {
+    const int64_t nblocks = rows * (cols / 32);
+    const int64_t grid = (nblocks + 255) / 256;
+    hipLaunchKernelGGL((quant_row_kernel<H, MODE>), dim3((unsigned)grid), blk, 0, st,
+                       static_cast<const uint4*>(src), nblocks, static_cast<uint4*>(nib),
+                       static_cast<uint8_t*>(sc));
+  } else if (axis == 1) {
+    if (cols % 8 == 0) {
+      const int64_t grid = ((rows / 32 + 3) / 4) * ((cols + 511) / 512);
+      hipLaunchKernelGGL((quant_col_kernel<H, MODE>), dim3((unsigned)grid), blk, 0, st,
+                         static_cast<const uint16_t*>(src), rows, cols,
+                         static_cast<uint8_t*>(nib), static_cast<uint8_t*>(sc));
+    } else {
+      const int64_t grid = (rows / 32) * ((cols + 255) / 256);
+      hipLaunchKernelGGL((quant_col_scalar_kernel<H, MODE>), dim3((unsigned)grid), blk, 0, st,
+                         static_cast<const uint16_t*>(src), rows, cols,
+                         static_cast<uint8_t*>(nib), static_cast<uint8_t*>(sc));
+    }
+  } else {
+    const int64_t grid = (rows / 32) * ((cols / 32 + 7) / 8);
+    hipLaunchKernelGGL((quant_2d_kernel<H, MODE>), dim3((unsigned)grid), blk, 0, st,
+                       static_cast<const uint16_t*>(src), rows, cols,
+                       static_cast<uint8_t*>(nib), static_cast<uint8_t*>(sc));
+  }
+  return hipGetLastError();
+}
+
+template <int H>
+hipError_t dispatch_mode(const void* src, int64_t rows, int64_t cols, int axis, int mode,
+                         void* nib, void* sc, hipStream_t st) {
+  return mode == kCeil ? dispatch_axis<H, kCeil>(src, rows, cols, axis, nib, sc, st)
+                       : dispatch_axis<H, kOcpFloor>(src, rows, cols, axis, nib, sc, st);
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* src, int64_t rows, int64_t cols, int axis, int hadamard,
+                           int scale_mode, void* nib, void* sc, hipStream_t stream) {
+  switch (hadamard) {
+    case 16: return dispatch_mode<16>(src, rows, cols, axis, scale_mode, nib, sc, stream);
+    case 32: return dispatch_mode<32>(src, rows, cols, axis, scale_mode, nib, sc, stream);
+    default: return dispatch_mode<0>(src, rows, cols, axis, scale_mode, nib, sc, stream);
+  }
+}
+
+}  // namespace mx

@@ -58,7 +58,8 @@ C_H32 = np.uint32(0x3E3504F3).view(np.float32)
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     """bf16 bit patterns -> fp32 values, exactly (a 16-bit left shift)."""
-    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return np.left_shift(np.asarray(bits, dtype=np.uint16).astype(np.uint32),
+                         np.uint32(16)).view(np.float32)
 
 
 # --------------------------------------------------------------------------

@@ -5,8 +5,10 @@ It draws random numbers and rounds them to bf16; it holds none of the
 method's arithmetic (no rotation, no scaling, no quantization).
 
 Recipe (all draws from ``numpy.random.default_rng(seed)``, PCG64, in the
-order listed; draws are fp64, rounded to fp32, then to bf16 with
-round-to-nearest-even; row-major):
+order listed; normal draws are numpy's float32 ziggurat
+(``standard_normal(dtype=float32)`` times sigma in fp32), the other
+distributions are drawn in fp64 and rounded to fp32; every tensor is then
+rounded to bf16 with round-to-nearest-even; row-major):
 
 =====  ====  =============================================================
 name   seed  tensors
@@ -40,23 +42,28 @@ __all__ = ["f64_to_bf16_bits", "bf16_bits_to_f32", "make", "WORKLOADS"]
 
 
 def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """fp64 -> fp32 (RNE) -> bf16 (RNE) bit patterns. Inputs are finite."""
+    """fp64/fp32 -> fp32 (RNE) -> bf16 (RNE) bit patterns. Inputs are finite."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    lsb = (u >> 16) & 1
-    return ((u + np.uint32(0x7FFF) + lsb) >> 16).astype(np.uint16)
+    sixteen = np.uint32(16)
+    lsb = np.bitwise_and(np.right_shift(u, sixteen), np.uint32(1))
+    return np.right_shift(u + np.uint32(0x7FFF) + lsb, sixteen).astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns to fp32."""
-    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return np.left_shift(np.asarray(b, dtype=np.uint16).astype(np.uint32),
+                         np.uint32(16)).view(np.float32)
 
 
 def _normal(rng, shape, sigma=1.0):
-    return rng.normal(0.0, sigma, size=shape)
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    return x
 
 
 def _rms_rows_with_outliers(rng, t, k, frac_count, factor):
-    z = _normal(rng, (t, k))
+    z = _normal(rng, (t, k)).astype(np.float64)
     idx = rng.choice(k, frac_count, replace=False)
     z[:, idx] *= factor
     rms = np.sqrt(np.mean(z * z, axis=1, keepdims=True))
@@ -66,7 +73,7 @@ def _rms_rows_with_outliers(rng, t, k, frac_count, factor):
 def _grad_with_spikes(rng, t, n):
     g = _normal(rng, (t, n), 1e-4)
     mask = rng.random((t, n)) < 1e-3
-    g[mask] *= 100.0
+    g[mask] *= np.float32(100.0)
     return g
 
 
@@ -79,7 +86,7 @@ def make(name: str, scale: int = 1) -> dict:
     """
     if name == "tiny":
         rng = np.random.default_rng(0)
-        x = _normal(rng, (128, 256))
+        x = _normal(rng, (128, 256)).astype(np.float64)
         w = _normal(rng, (256, 256))
         idx = rng.choice(256, 5, replace=False)
         x[:, idx] *= 40.0
@@ -110,9 +117,10 @@ def make(name: str, scale: int = 1) -> dict:
         t, n, k = 8192 // scale, 4096, 14336 // scale
         out = {"dY": f64_to_bf16_bits(_grad_with_spikes(rng, t, n))}
         g = _normal(rng, (t, k))
-        silu = g / (1.0 + np.exp(-g))
+        silu = g / (np.float32(1.0) + np.exp(-g))
         del g
-        out["X"] = f64_to_bf16_bits(silu * np.abs(rng.standard_cauchy(size=(t, k))))
+        silu *= np.abs(rng.standard_cauchy(size=(t, k))).astype(np.float32)
+        out["X"] = f64_to_bf16_bits(silu)
         return out
     raise KeyError(name)
 

@@ -1,0 +1,174 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, its enums match the binding, and argument validation
+returns the documented status before any HIP call (no kernel is launched
+by any call in this file)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_quantized_gemm_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp4.h")
+
+
+def header_text():
+    with open(HEADER) as f:
+        return f.read()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mx.LIB_PATH):
+        pytest.fail("libmxfp4.so is not built (run __graft_entry__.build())")
+    return mx.load_library()
+
+
+def test_header_declares_the_bound_functions():
+    decl = set(re.findall(r"\b(mxfp4_[a-z_0-9]+)\s*\(", re.sub(r"/\*.*?\*/", "", header_text(), flags=re.S)))
+    assert decl == set(mx.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    text = re.sub(r"/\*.*?\*/", "", header_text(), flags=re.S)
+    for name in set(re.findall(r"\b(mxfp4_[a-z_0-9]+)\s*\(", text)):
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_enums_match_binding():
+    text = header_text()
+    def val(name):
+        m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
+        assert m, name
+        return int(m.group(1))
+    assert val("MXFP4_AXIS_ROW") == mx.AXIS_ROW
+    assert val("MXFP4_AXIS_COL") == mx.AXIS_COL
+    assert val("MXFP4_AXIS_2D32") == mx.AXIS_2D32
+    assert val("MXFP4_SCALE_OCP_FLOOR") == mx.SCALE_OCP_FLOOR
+    assert val("MXFP4_SCALE_CEIL") == mx.SCALE_CEIL
+    assert val("MXFP4_OUT_F32") == mx.OUT_F32 and val("MXFP4_OUT_BF16") == mx.OUT_BF16
+    assert val("MXFP4_OP_FPROP") == mx.OP_FPROP and val("MXFP4_OP_WGRAD") == mx.OP_WGRAD
+
+
+def test_status_strings(lib):
+    names = ["MXFP4_OK", "MXFP4_ERR_NULL", "MXFP4_ERR_SHAPE", "MXFP4_ERR_MODE",
+             "MXFP4_ERR_WORKSPACE", "MXFP4_ERR_HIP", "MXFP4_ERR_ALIGN"]
+    for code, name in enumerate(names):
+        assert lib.mxfp4_status_string(code).decode() == name
+    assert lib.mxfp4_status_string(99).decode() == "MXFP4_ERR_UNKNOWN"
+    assert lib.mxfp4_status_string(-1).decode() == "MXFP4_ERR_UNKNOWN"
+
+
+def test_workspace_bytes(lib):
+    r = lambda x: (x + 255) // 256 * 256
+    T, N, K = 8192, 6144, 4096
+    want = r(T * K // 2) + r(T * K // 32) + r(N * K // 2) + r(N * K // 32)
+    assert lib.mxfp4_workspace_bytes(mx.OP_FPROP, T, N, K) == want
+    T, N, K = 8192, 4096, 14336
+    want = r(T * N // 2) + r(T * N // 32) + r(K * N // 2) + r(K * N // 32)
+    assert lib.mxfp4_workspace_bytes(mx.OP_DGRAD, T, N, K) == want
+    want = r(N * T // 2) + r(N * T // 32) + r(K * T // 2) + r(K * T // 32)
+    assert lib.mxfp4_workspace_bytes(mx.OP_WGRAD, T, N, K) == want
+    assert lib.mxfp4_workspace_bytes(mx.OP_FPROP, 10, 10, 33) == 0  # K % 32
+    assert lib.mxfp4_workspace_bytes(mx.OP_DGRAD, 10, 33, 10) == 0  # N % 32
+    assert lib.mxfp4_workspace_bytes(mx.OP_WGRAD, 33, 10, 10) == 0  # T % 32
+    assert lib.mxfp4_workspace_bytes(7, 32, 32, 32) == 0
+    assert lib.mxfp4_workspace_bytes(mx.OP_FPROP, 0, 32, 32) == 0
+
+
+FAKE = ctypes.c_void_p(0x10000)   # aligned non-null address; never dereferenced
+FAKE_ODD = ctypes.c_void_p(0x10008)
+NULL = ctypes.c_void_p(0)
+
+
+def q(lib, src=FAKE, rows=64, cols=64, axis=0, h=16, mode=0, nib=FAKE, sc=FAKE):
+    return lib.mxfp4_quantize(src, rows, cols, axis, h, mode, nib, sc, NULL)
+
+
+def test_quantize_validation(lib):
+    assert q(lib, axis=3) == 3
+    assert q(lib, axis=-1) == 3
+    assert q(lib, h=8) == 3
+    assert q(lib, mode=2) == 3
+    assert q(lib, cols=48) == 2                # row axis: cols % 32
+    assert q(lib, axis=1, rows=48) == 2        # col axis: rows % 32
+    assert q(lib, axis=2, rows=48) == 2        # 2D: both % 32
+    assert q(lib, axis=2, cols=40) == 2
+    assert q(lib, rows=-32) == 2
+    assert q(lib, src=NULL) == 1
+    assert q(lib, nib=NULL) == 1
+    assert q(lib, sc=NULL) == 1
+    assert q(lib, src=FAKE_ODD) == 6
+    assert q(lib, nib=FAKE_ODD) == 6
+    # empty inputs are valid and launch nothing, even with NULL buffers
+    assert q(lib, rows=0, src=NULL, nib=NULL, sc=NULL) == 0
+    assert q(lib, cols=0, src=NULL, nib=NULL, sc=NULL) == 0
+    assert q(lib, axis=1, cols=0, src=NULL, nib=NULL, sc=NULL) == 0
+
+
+def g(lib, M=64, N=64, K=64, out=0, A=FAKE, As=FAKE, B=FAKE, Bs=FAKE, C=FAKE):
+    return lib.mxfp4_gemm(A, As, B, Bs, M, N, K, C, out, NULL)
+
+
+def test_gemm_validation(lib):
+    assert g(lib, out=2) == 3
+    assert g(lib, M=0) == 2
+    assert g(lib, N=0) == 2
+    assert g(lib, K=0) == 2
+    assert g(lib, K=48) == 2
+    assert g(lib, K=16) == 2
+    assert g(lib, A=NULL) == 1
+    assert g(lib, Bs=NULL) == 1
+    assert g(lib, C=NULL) == 1
+    assert g(lib, A=FAKE_ODD) == 6
+    assert g(lib, C=ctypes.c_void_p(0x10002)) == 6             # fp32 C needs 4 B alignment
+    assert g(lib, C=ctypes.c_void_p(0x10001), out=1) == 6      # bf16 C needs 2 B alignment
+
+
+@pytest.mark.parametrize("name", ["mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad"])
+def test_fused_validation(lib, name):
+    fn = getattr(lib, name)
+    T, N, K = 64, 64, 64
+    op = {"mxfp4_fprop": 0, "mxfp4_dgrad": 1, "mxfp4_wgrad": 2}[name]
+    need = lib.mxfp4_workspace_bytes(op, T, N, K)
+    assert need > 0
+    call = lambda **kw: fn(kw.get("P", FAKE), kw.get("Q", FAKE), kw.get("T", T), kw.get("N", N),
+                           kw.get("K", K), kw.get("h", 16), kw.get("mode", 0),
+                           kw.get("ws", FAKE), kw.get("wsb", need), kw.get("out", FAKE),
+                           kw.get("od", 0), NULL)
+    assert call(h=4) == 3
+    assert call(mode=5) == 3
+    assert call(od=9) == 3
+    assert call(T=0) == 2
+    bad_axis = {"mxfp4_fprop": "K", "mxfp4_dgrad": "N", "mxfp4_wgrad": "T"}[name]
+    assert call(**{bad_axis: 40}) == 2
+    assert call(P=NULL) == 1
+    assert call(ws=NULL) == 1
+    assert call(out=NULL) == 1
+    assert call(wsb=need - 1) == 4
+    assert call(P=FAKE_ODD) == 6
+    assert call(ws=ctypes.c_void_p(0x10010)) == 6   # workspace must be 256 B aligned
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    saved = mx._LIB
+    try:
+        mx._LIB = None
+        with pytest.raises(RuntimeError, match="missing"):
+            mx.load_library(str(tmp_path / "missing.so"))
+    finally:
+        mx._LIB = saved
+
+
+def test_product_path_does_not_import_oracle():
+    """The package and its sources never reference the oracle."""
+    pkg = os.path.dirname(mx.__file__)
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".cpp", ".h")):
+                with open(os.path.join(dirpath, fn)) as f:
+                    text = f.read()
+                assert not re.search(r"\boracle\b", text), fn

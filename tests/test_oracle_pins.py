@@ -45,7 +45,7 @@ def sylvester(h):
 
 def all_bf16_f32(finite_only=True):
     bits = np.arange(65536, dtype=np.uint32)
-    v = (bits << 16).view(np.float32)
+    v = np.left_shift(bits, np.uint32(16)).view(np.float32)
     return v[np.isfinite(v)] if finite_only else v
 
 
