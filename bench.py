@@ -1,0 +1,340 @@
+#!/usr/bin/env python3
+"""Benchmark of the H16 + MXFP4 quantize + MXFP4 GEMM hot path on one MI355X.
+
+One step = the four linear-layer products of a Llama-3.1-8B block at 8192
+tokens, each as the three launches its fused entry point issues (quantize
+A, quantize B, MXFP4 GEMM) through the C ABI, on one stream:
+
+  qkv fprop         Y  = X W^T      GEMM (M, N, K) = (8192, 6144, 4096)
+  gate+up fprop     Y  = X W^T      (8192, 28672, 4096)
+  down-proj dgrad   dX = dY W       (8192, 14336, 4096)   W quantized 32x1
+  down-proj wgrad   dW = dY^T X     (4096, 14336, 8192)   both 32x1 along T
+
+H16 rotation along each reduction axis, OCP-floor scales, fp32 output.
+Inputs are seeded synthetic tensors (synthetic.make) already resident in
+HBM when the timed region starts. HIP events bracket every launch in the
+timed region, giving per-kernel average durations; `value` is the step's
+total 2MNK over its wall time. The fused entry points are timed as well
+(same kernels, no inner events) as a cross-check.
+
+Also measured: the quantizer-only workload (8192 x 4096, Student-t x
+log-normal) for every axis and scale rule with H16, plus H0/H32 row-wise,
+cycling six buffer sets (> 400 MB) so the 256 MB last-level cache cannot
+hold the data, reported in GB/s of algorithmic bytes (2 B read + 0.5 B
+nibbles + 1/32 B scale per element).
+
+The CPU baseline is the oracle (numpy, fp64 GEMM) timed on this host on a
+bounded sample of the same step.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "H16+MXFP4 quant+GEMM TFLOP/s (Llama-8B Fprop/Dgrad/Wgrad); quantizer GB/s"
+HBM_PEAK_GBS = 8000.0
+MXFP4_PEAK_TFLOPS = 10100.0
+
+# name, workload, op, (T, N, K), source tensors (P, Q)
+PRODUCTS = [
+    ("qkv_fprop", "qkv", "fprop", (8192, 6144, 4096), ("X", "W")),
+    ("gateup_fprop", "mlp", "fprop", (8192, 28672, 4096), ("X", "W_gu")),
+    ("down_dgrad", "mlp", "dgrad", (8192, 4096, 14336), ("dY", "W_down")),
+    ("down_wgrad", "wgrad", "wgrad", (8192, 4096, 14336), ("dY", "X")),
+]
+DOMINANT = "gateup_fprop"
+
+
+def plan(op, T, N, K):
+    """(A source shape, A axis), (B source shape, B axis), GEMM (M, N, K)."""
+    if op == "fprop":
+        return ((T, K), 0), ((N, K), 0), (T, N, K)
+    if op == "dgrad":
+        return ((T, N), 0), ((N, K), 1), (T, K, N)
+    return ((T, N), 1), ((T, K), 1), (N, K, T)
+
+
+def quant_bytes(rows, cols, axis):
+    n = rows * cols
+    return 2 * n + n // 2 + (n // 1024 if axis == 2 else n // 32)
+
+
+def sha_of(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_src):
+    """HBM bytes per launch of the dominant GEMM from the committed counter
+    summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "gemm_gateup_fprop_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha") != sha_of(kernel_src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(work, budget_rows=1024, budget_cols=4096):
+    """Oracle on a bounded sample of the step: for each product, a
+    budget_rows x budget_cols tile of the output at full reduction length
+    (quantize the matching source slices, dequantize, fp64 GEMM + sum|a||b|)."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    flops = 0.0
+    t0 = time.perf_counter()
+    for name, wl, op, (T, N, K), (pn, qn) in PRODUCTS:
+        P, Q = work[wl][pn], work[wl][qn]
+        (_, _), (_, _), (GM, GN, GK) = plan(op, T, N, K)
+        m, n = min(budget_rows, GM), min(budget_cols, GN)
+        if op == "fprop":
+            qa = O.quantize(P[:m], O.AXIS_ROW, 16, 0)
+            qb = O.quantize(Q[:n], O.AXIS_ROW, 16, 0)
+        elif op == "dgrad":
+            qa = O.quantize(P[:m], O.AXIS_ROW, 16, 0)
+            qb = O.quantize(np.ascontiguousarray(Q[:, :n]), O.AXIS_COL, 16, 0)
+        else:
+            qa = O.quantize(np.ascontiguousarray(P[:, :m]), O.AXIS_COL, 16, 0)
+            qb = O.quantize(np.ascontiguousarray(Q[:, :n]), O.AXIS_COL, 16, 0)
+        O.gemm_ref(O.dequantize(*qa), O.dequantize(*qb))
+        flops += 2.0 * m * n * GK
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"{budget_rows}x{budget_cols} output tile of each of the 4 products at full "
+                      f"reduction length: oracle rotate+quantize of the matching source slices, "
+                      f"dequantize, fp64 GEMM and sum|a||b| (numpy; BLAS threads = {cores})"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-quantizer", action="store_true")
+    ap.add_argument("--quant-iters", type=int, default=30)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path has no multi-GPU component; see the sharding note in the design doc)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mxfp4_quantized_gemm_amd as mx
+    import synthetic
+
+    mx.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- inputs
+    t0 = time.perf_counter()
+    work = {wl: synthetic.make(wl) for wl in ("qkv", "mlp", "wgrad")}
+    log(f"inputs generated in {time.perf_counter() - t0:.1f}s")
+    dev_t = {}
+    for wl, d in work.items():
+        for k, v in d.items():
+            dev_t[(wl, k)] = torch.from_numpy(v.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    prods = []
+    for name, wl, op, (T, N, K), (pn, qn) in PRODUCTS:
+        (sa, axa), (sb, axb), (GM, GN, GK) = plan(op, T, N, K)
+        na, sca = mx.packed_shapes(sa[0], sa[1], axa)
+        nb, scb = mx.packed_shapes(sb[0], sb[1], axb)
+        opcode = {"fprop": mx.OP_FPROP, "dgrad": mx.OP_DGRAD, "wgrad": mx.OP_WGRAD}[op]
+        prods.append(dict(
+            name=name, op=op, T=T, N=N, K=K, opcode=opcode, GM=GM, GN=GN, GK=GK,
+            P=dev_t[(wl, pn)], Q=dev_t[(wl, qn)], sa=sa, axa=axa, sb=sb, axb=axb,
+            an=torch.empty(na, dtype=torch.uint8, device=dev),
+            asc=torch.empty(sca, dtype=torch.uint8, device=dev),
+            bn=torch.empty(nb, dtype=torch.uint8, device=dev),
+            bsc=torch.empty(scb, dtype=torch.uint8, device=dev),
+            C=torch.empty((GM, GN), dtype=torch.float32, device=dev),
+            ws=torch.empty(mx.mxfp4_workspace_bytes(opcode, T, N, K), dtype=torch.uint8,
+                           device=dev),
+        ))
+
+    def launches(p):
+        return [
+            lambda: mx.mxfp4_quantize(p["P"], p["sa"][0], p["sa"][1], p["axa"], 16, 0, p["an"],
+                                      p["asc"], stream),
+            lambda: mx.mxfp4_quantize(p["Q"], p["sb"][0], p["sb"][1], p["axb"], 16, 0, p["bn"],
+                                      p["bsc"], stream),
+            lambda: mx.mxfp4_gemm(p["an"], p["asc"], p["bn"], p["bsc"], p["GM"], p["GN"], p["GK"],
+                                  p["C"], mx.OUT_F32, stream),
+        ]
+
+    seq = [(p, j, fn) for p in prods for j, fn in enumerate(launches(p))]
+
+    # ---------------------------------------------------------------- warmup
+    for _ in range(args.warmup):
+        for _, _, fn in seq:
+            fn()
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------- timed region
+    K_ = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)] for _ in range(K_)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(K_):
+        ev[s][0].record(stream)
+        for i, (_, _, fn) in enumerate(seq):
+            fn()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    kernel_ms = np.zeros(len(seq))
+    step_ms = []
+    for s in range(K_):
+        d = [ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(len(seq))]
+        kernel_ms += np.array(d)
+        step_ms.append(ev[s][0].elapsed_time(ev[s][-1]))
+    kernel_ms /= K_
+    ms_per_step = wall * 1e3 / K_
+    total_flops = sum(2.0 * p["GM"] * p["GN"] * p["GK"] for p in prods)
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+
+    per_product = {}
+    kernels = []
+    for idx, (p, j, _) in enumerate(seq):
+        name = p["name"]
+        rec = per_product.setdefault(name, {"GEMM_MNK": [p["GM"], p["GN"], p["GK"]]})
+        if j < 2:
+            shape, axis = (p["sa"], p["axa"]) if j == 0 else (p["sb"], p["axb"])
+            b = quant_bytes(shape[0], shape[1], axis)
+            gbs = b / (kernel_ms[idx] * 1e-3) / 1e9
+            rec["quant_" + "AB"[j] + "_us"] = round(kernel_ms[idx] * 1e3, 2)
+            rec["quant_" + "AB"[j] + "_GBs"] = round(gbs, 1)
+            kernels.append({"kernel": f"{name}.quant_{'AB'[j]}", "axis": ["row", "col", "2d"][axis],
+                            "us": round(kernel_ms[idx] * 1e3, 2), "GB/s": round(gbs, 1),
+                            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
+        else:
+            f = 2.0 * p["GM"] * p["GN"] * p["GK"]
+            tf = f / (kernel_ms[idx] * 1e-3) / 1e12
+            rec["gemm_us"] = round(kernel_ms[idx] * 1e3, 2)
+            rec["gemm_TFLOPs"] = round(tf, 1)
+            tot = kernel_ms[idx - 2] + kernel_ms[idx - 1] + kernel_ms[idx]
+            rec["fused_TFLOPs"] = round(f / (tot * 1e-3) / 1e12, 1)
+            kernels.append({"kernel": f"{name}.gemm", "us": round(kernel_ms[idx] * 1e3, 2),
+                            "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / MXFP4_PEAK_TFLOPS, 4)})
+    log(f"step {ms_per_step:.3f} ms, {value:.1f} TFLOP/s")
+
+    # fused entry points, same work, no inner events (cross-check)
+    def fused_step():
+        for p in prods:
+            fn = {"fprop": mx.mxfp4_fprop, "dgrad": mx.mxfp4_dgrad, "wgrad": mx.mxfp4_wgrad}[p["op"]]
+            fn(p["P"], p["Q"], p["T"], p["N"], p["K"], 16, 0, p["ws"], p["C"], mx.OUT_F32, stream)
+    for _ in range(2):
+        fused_step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K_):
+        fused_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fused_ms = e0.elapsed_time(e1) / K_
+
+    # -------------------------------------------------- quantizer workload
+    quant = None
+    if not args.no_quantizer:
+        A = synthetic.make("quant")["A"]
+        nsets = 6
+        srcs = [torch.from_numpy(A.view(np.int16)).to(dev).view(torch.bfloat16)]
+        for i in range(1, nsets):
+            srcs.append(srcs[0].clone())
+        R, Cc = A.shape
+        quant = {}
+        arms = [(ax, 16, m) for ax in (0, 1, 2) for m in (0, 1)] + [(0, 0, 0), (0, 32, 0)]
+        for ax, h, m in arms:
+            ns_, ss_ = mx.packed_shapes(R, Cc, ax)
+            outs = [(torch.empty(ns_, dtype=torch.uint8, device=dev),
+                     torch.empty(ss_, dtype=torch.uint8, device=dev)) for _ in range(nsets)]
+            for i in range(nsets):
+                mx.mxfp4_quantize(srcs[i], R, Cc, ax, h, m, outs[i][0], outs[i][1], stream)
+            torch.cuda.synchronize()
+            its = args.quant_iters
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(its + 1)]
+            evs[0].record(stream)
+            for i in range(its):
+                k = i % nsets
+                mx.mxfp4_quantize(srcs[k], R, Cc, ax, h, m, outs[k][0], outs[k][1], stream)
+                evs[i + 1].record(stream)
+            torch.cuda.synchronize()
+            d = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(its)])
+            b = quant_bytes(R, Cc, ax)
+            key = f"{['row', 'col', '2d'][ax]}_h{h}_{['ocp_floor', 'ceil'][m]}"
+            quant[key] = {"us_median": round(float(np.median(d)) * 1e3, 2),
+                          "GB/s": round(b / (np.median(d) * 1e-3) / 1e9, 1),
+                          "GB/s_best": round(b / (d.min() * 1e-3) / 1e9, 1)}
+            quant[key]["frac_hbm"] = round(quant[key]["GB/s"] / HBM_PEAK_GBS, 4)
+            del outs
+        if "row_h16_ocp_floor" in quant and "row_h32_ocp_floor" in quant:
+            quant["h16_over_h32_row"] = round(quant["row_h16_ocp_floor"]["GB/s"] /
+                                              quant["row_h32_ocp_floor"]["GB/s"], 3)
+        log("quantizer arms done")
+
+    # -------------------------------------------------------------- roofline
+    dom = [k for k in kernels if k["kernel"] == f"{DOMINANT}.gemm"][0]
+    dp = [p for p in prods if p["name"] == DOMINANT][0]
+    gemm_src = os.path.join(ROOT, "mxfp4_quantized_gemm_amd", "csrc", "gemm.hip")
+    roofline = {"kernel": f"mxfp4 GEMM {DOMINANT} (M,N,K)=({dp['GM']},{dp['GN']},{dp['GK']})",
+                "bound": "mfma", "achieved": dom["TFLOP/s"], "peak": MXFP4_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(dom["TFLOP/s"] / MXFP4_PEAK_TFLOPS, 4),
+                "traffic": load_traffic(gemm_src)}
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(work)
+    if cpu:
+        log(f"cpu baseline {cpu['value']:.4f} TFLOP/s in {cpu['seconds']} s")
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K_, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": "llama3.1-8b linear products at 8192 tokens: qkv fprop "
+                               "(T,N,K)=(8192,6144,4096), mlp gate+up fprop (8192,28672,4096), "
+                               "down-proj dgrad (8192,4096,14336), down-proj wgrad "
+                               "(8192,4096,14336); H16 along each reduction axis, 1x32 row / "
+                               "32x1 col blocks, ocp_floor scales, fp32 out",
+                   "hadamard": 16, "scale_mode": "ocp_floor", "out_dtype": "f32",
+                   "parallelism": "single-gpu"},
+        "fused_entry_ms_per_step": round(fused_ms, 4),
+        "event_step_ms_median": round(float(np.median(step_ms)), 4),
+        "products": per_product,
+        "kernels": kernels,
+        "quantizer": quant,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
