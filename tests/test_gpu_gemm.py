@@ -54,6 +54,10 @@ SHAPES = [
     (256, 384, 4096),    # Llama reduction length
     (200, 300, 544),
     (512, 512, 1024),    # several full tiles in every direction
+    (1, 1, 256),         # large-tile kernel, one element
+    (300, 200, 512),     # large-tile kernel, ragged M and N
+    (1000, 600, 768),    # large-tile kernel, several ragged tiles, odd k-tile pairs
+    (768, 1024, 2048),
 ]
 
 
