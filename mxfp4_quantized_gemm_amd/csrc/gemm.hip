@@ -448,6 +448,19 @@ __device__ __forceinline__ void compute(const uint8_t* st, v16f (&acc)[TN][TM], 
   }
 }
 
+// Ordering point: every MFMA issued so far must have been issued before any
+// later memory operation. MFMAs touch no memory, so without this the
+// compiler may sink a k-tile's MFMAs below the next LDS stores and barrier,
+// which leaves the global-load latency of the prefetch uncovered. The empty
+// asm reads the accumulators (in AGPRs) and clobbers memory.
+template <int TM, int TN>
+__device__ __forceinline__ void order_after_mfma(v16f (&acc)[TN][TM]) {
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int i = 0; i < TM; ++i) asm volatile("" ::"a"(acc[j][i]) : "memory");
+}
+
 // Work-group id -> output tile. Consecutive work-group ids are dispatched
 // round-robin over the 8 XCDs; the remap gives each XCD a contiguous range
 // of logical tiles, walked in groups of GROUP_M tile-rows so that the tiles
@@ -466,7 +479,7 @@ __device__ __forceinline__ void tile_of(int64_t wg, int64_t nwg, int64_t ntm, in
   tn = r / gs;
 }
 
-template <int WM, int WN, int TM, int TN, int KB, int NS, int WPE, int OUT, bool VEC>
+template <int WM, int WN, int TM, int TN, int KB, int NS, int WPE, int OUT, bool VEC, int KROT = 4>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WM * WN, 64 * WM * WN),
                           amdgpu_waves_per_eu(WPE)))
 void gemm_big_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
@@ -498,34 +511,44 @@ void gemm_big_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   // (redundant) loads at the end land in a buffer nobody reads again.
   Offs<G> O;
   make_offsets<G>(O, m0, n0, M, N, kbytes, kblk, t);
+  // Each tile walks its k-tiles starting at its own offset: operand rows have
+  // a power-of-two pitch, so tiles in lockstep at the same k would all load
+  // from the same few L2 channels. (The sum order per output is fixed per
+  // tile, so results stay deterministic.)
+  const int kofs = (int)(((tm * ntn + tn) * KROT) % nkt);
+  auto kk = [&](int k) { return (k + kofs) % nkt; };
   if (NS == 2) {
     Regs<G> R0, R1;
-    gload<G>(R0, O, A, As, B, Bs, 0);
-    gload<G>(R1, O, A, As, B, Bs, min(1, nkt - 1));
+    gload<G>(R0, O, A, As, B, Bs, kk(0));
+    gload<G>(R1, O, A, As, B, Bs, kk(min(1, nkt - 1)));
     lstore<G>(R0, lds, t);
     lds_barrier();
     for (int kt = 0; kt < nkt; kt += 2) {
-      gload<G>(R0, O, A, As, B, Bs, min(kt + 2, nkt - 1));
+      gload<G>(R0, O, A, As, B, Bs, kk(min(kt + 2, nkt - 1)));
       compute<G, TM, TN>(lds, acc, arow0, brow0, lane);
+      order_after_mfma<TM, TN>(acc);
       lstore<G>(R1, lds + G::STAGE, t);
       lds_barrier();
-      gload<G>(R1, O, A, As, B, Bs, min(kt + 3, nkt - 1));
+      gload<G>(R1, O, A, As, B, Bs, kk(min(kt + 3, nkt - 1)));
       compute<G, TM, TN>(lds + G::STAGE, acc, arow0, brow0, lane);
+      order_after_mfma<TM, TN>(acc);
       lstore<G>(R0, lds, t);
       lds_barrier();
     }
   } else {
     Regs<G> R;
-    gload<G>(R, O, A, As, B, Bs, 0);
+    gload<G>(R, O, A, As, B, Bs, kk(0));
     lstore<G>(R, lds, t);
     lds_barrier();
     for (int kt = 0; kt < nkt; kt += 2) {
-      gload<G>(R, O, A, As, B, Bs, min(kt + 1, nkt - 1));
+      gload<G>(R, O, A, As, B, Bs, kk(min(kt + 1, nkt - 1)));
       compute<G, TM, TN>(lds, acc, arow0, brow0, lane);
+      order_after_mfma<TM, TN>(acc);
       lstore<G>(R, lds + G::STAGE, t);
       lds_barrier();
-      gload<G>(R, O, A, As, B, Bs, min(kt + 2, nkt - 1));
+      gload<G>(R, O, A, As, B, Bs, kk(min(kt + 2, nkt - 1)));
       compute<G, TM, TN>(lds + G::STAGE, acc, arow0, brow0, lane);
+      order_after_mfma<TM, TN>(acc);
       lstore<G>(R, lds, t);
       lds_barrier();
     }
@@ -611,6 +634,7 @@ hipError_t launch(const uint8_t* a, const uint8_t* as, const uint8_t* b, const u
 }
 
 }  // namespace big
+
 }  // namespace
 
 hipError_t launch_gemm(const void* Aq, const void* As, const void* Bq, const void* Bs, int64_t M,
@@ -620,9 +644,16 @@ hipError_t launch_gemm(const void* Aq, const void* As, const void* Bq, const voi
   const auto* b = static_cast<const uint8_t*>(Bq);
   const auto* bs = static_cast<const uint8_t*>(Bs);
   const dim3 blk(256);
-  // Large-tile path: K a multiple of two 128-deep k-tiles and 4-byte
-  // aligned scale arrays.
-  if (K % 256 == 0 && ((uintptr_t)As % 4 == 0) && ((uintptr_t)Bs % 4 == 0))
+  // Large-tile paths (the main loop runs k-tiles in pairs, so K must hold
+  // an even number of them; 32-bit per-lane operand offsets):
+  //  K % 512 == 0: 256 x 256 tile, 8 waves of 128 x 64, 256-deep k-tiles
+  //                (whole 128-byte operand rows per k-tile);
+  //  K % 256 == 0: 256 x 256 tile, 4 waves of 128 x 128, 128-deep k-tiles.
+  const bool off32 = (M * (K / 2) < (int64_t(1) << 32)) && (N * (K / 2) < (int64_t(1) << 32));
+  const bool sc_al = ((uintptr_t)As % 8 == 0) && ((uintptr_t)Bs % 8 == 0);
+  if (off32 && sc_al && K % 512 == 0)
+    return big::launch<2, 4, 4, 2, 128, 1, 2>(a, as, b, bs, M, N, K, C, out_dtype, stream);
+  if (off32 && sc_al && K % 256 == 0)
     return big::launch<2, 2, 4, 4, 64, 2, 1>(a, as, b, bs, M, N, K, C, out_dtype, stream);
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const bool svec = (K % 256 == 0) && ((uintptr_t)As % 8 == 0) && ((uintptr_t)Bs % 8 == 0);
