@@ -15,7 +15,9 @@
 // E8M0 byte of that 32-block in the byte of its scale register picked by
 // op_sel. Output lane l, register r holds C[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32].
 //
-// Tiling: a 256-thread work-group (4 waves, 2 x 2) computes a 128 x 128
+// Two kernel families. The large-tile kernels (namespace big, below) serve
+// K % 256 == 0. The general kernel here serves any K % 32 == 0 and any M, N:
+// a 256-thread work-group (4 waves, 2 x 2) computes a 128 x 128
 // tile of C; each wave a 64 x 64 sub-tile (2 x 2 MFMA tiles, 64 fp32
 // accumulators per lane). The k-loop steps 256 elements (128 bytes of
 // nibbles per row, 8 scale bytes per row). Tiles of A and B are staged in
