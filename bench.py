@@ -130,6 +130,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true")
     ap.add_argument("--quant-iters", type=int, default=30)
+    ap.add_argument("--pmc-gemm", action="store_true",
+                    help="counter-collection mode: run only the gate+up GEMM (3 launches) and a "
+                         "1 GiB device-to-device copy (3 launches, the calibration kernel)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -151,6 +154,24 @@ def main():
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.pmc_gemm:
+        mlp = synthetic.make("mlp")
+        x = torch.from_numpy(mlp["X"].view(np.int16)).to(dev).view(torch.bfloat16)
+        w = torch.from_numpy(mlp["W_gu"].view(np.int16)).to(dev).view(torch.bfloat16)
+        an, asc = mx.quantize(x, mx.AXIS_ROW, 16, 0)
+        bn, bsc = mx.quantize(w, mx.AXIS_ROW, 16, 0)
+        c = torch.empty((8192, 28672), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            mx.mxfp4_gemm(an, asc, bn, bsc, 8192, 28672, 4096, c, mx.OUT_F32, stream)
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("pmc-gemm done: 3 gate+up GEMMs, 3 copies of 1 GiB")
+        return
 
     # ---------------------------------------------------------------- inputs
     t0 = time.perf_counter()

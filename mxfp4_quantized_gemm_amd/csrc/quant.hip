@@ -188,6 +188,8 @@ __global__ __launch_bounds__(256) void quant_2d_kernel(const uint16_t* __restric
 }
 
 // ------------------------------------------------------ column (32x1, transposed)
+// Three paths: staged (below, rows % 128 == 0), vector (cols % 8 == 0) and
+// scalar (any cols).
 // Vector path (cols % 8 == 0). Work-group = 4 waves; the flat grid walks
 // (row group of 128, column group of 512) with the column group fastest.
 // Lane l of wave w owns columns [c0, c0 + 8), c0 = group*512 + 8l, for the
@@ -236,6 +238,71 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
   }
 }
 
+// Staged path (rows % 128 == 0, cols % 4 == 0, 4-byte aligned scales):
+// work-group = 4 waves = 4 bands of 32 rows (a 128-row group) x 256 columns.
+// Lane l of wave w owns columns [c0, c0 + 4), c0 = group*256 + 4l, of band
+// 4*rowgroup + w and loads them with 32 8-byte loads (a wave reads 512
+// contiguous bytes per row). The quantized bands go to LDS; the work-group
+// then writes each column's 4 bands as 64 contiguous nibble bytes and one
+// 4-byte scale word, instead of scattered 16-byte and 1-byte stores. Four
+// columns per lane keep the register count low enough for four waves per
+// SIMD, so loads of one wave overlap the arithmetic of another.
+template <int H, int MODE>
+__global__ __launch_bounds__(256) void quant_col_staged_kernel(const uint16_t* __restrict__ src,
+                                                               int64_t rows, int64_t cols,
+                                                               uint8_t* __restrict__ nib,
+                                                               uint8_t* __restrict__ sc) {
+  __shared__ __attribute__((aligned(16))) uint8_t onib[256 * 4 * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t osc[256 * 4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t ncg = (cols + 255) / 256;
+  const int64_t cg = (int64_t)blockIdx.x % ncg;
+  const int64_t rg = (int64_t)blockIdx.x / ncg;
+  const int64_t band = rg * 4 + wave;
+  const int64_t c0 = cg * 256 + (int64_t)lane * 4;
+  if (c0 < cols) {
+    const uint16_t* p = src + band * 32 * cols + c0;
+    uint2 raw[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) raw[r] = *reinterpret_cast<const uint2*>(p + r * cols);
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      float a[32], b[32];
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        const uint32_t d = pr == 0 ? raw[r].x : raw[r].y;
+        a[r] = bf16lo(d);
+        b[r] = bf16hi(d);
+      }
+      hadamard32<H>(a);
+      hadamard32<H>(b);
+      uint4 na, nb;
+      uint32_t sa, sb;
+      encode_block<MODE>(a, na, sa);
+      encode_block<MODE>(b, nb, sb);
+      const int ca = lane * 4 + 2 * pr, cb = ca + 1;
+      *reinterpret_cast<uint4*>(onib + (ca * 4 + wave) * 16) = na;
+      *reinterpret_cast<uint4*>(onib + (cb * 4 + wave) * 16) = nb;
+      osc[ca * 4 + wave] = (uint8_t)sa;
+      osc[cb * 4 + wave] = (uint8_t)sb;
+    }
+  }
+  __syncthreads();
+  const int64_t npitch = rows / 2, spitch = rows / 32;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = threadIdx.x + 256 * i;  // 16-byte chunk: column q / 4, band q % 4
+    const int64_t col = cg * 256 + (q >> 2);
+    if (col < cols)
+      *reinterpret_cast<uint4*>(nib + col * npitch + rg * 64 + (q & 3) * 16) =
+          *reinterpret_cast<const uint4*>(onib + q * 16);
+  }
+  const int64_t col = cg * 256 + threadIdx.x;
+  if (col < cols)
+    *reinterpret_cast<uint32_t*>(sc + col * spitch + rg * 4) =
+        *reinterpret_cast<const uint32_t*>(osc + threadIdx.x * 4);
+}
+
 // Scalar path for any cols: one thread per (column, 32-row band); loads are
 // 2-byte, coalesced across the threads of a row.
 template <int H, int MODE>
@@ -269,7 +336,12 @@ hipError_t dispatch_axis(const void* src, int64_t rows, int64_t cols, int axis, 
                        static_cast<const uint4*>(src), nblocks, static_cast<uint4*>(nib),
                        static_cast<uint8_t*>(sc));
   } else if (axis == 1) {
-    if (cols % 8 == 0) {
+    if (rows % 128 == 0 && cols % 4 == 0 && ((uintptr_t)sc % 4 == 0)) {
+      const int64_t grid = (rows / 128) * ((cols + 255) / 256);
+      hipLaunchKernelGGL((quant_col_staged_kernel<H, MODE>), dim3((unsigned)grid), blk, 0, st,
+                         static_cast<const uint16_t*>(src), rows, cols,
+                         static_cast<uint8_t*>(nib), static_cast<uint8_t*>(sc));
+    } else if (cols % 8 == 0) {
       const int64_t grid = ((rows / 32 + 3) / 4) * ((cols + 511) / 512);
       hipLaunchKernelGGL((quant_col_kernel<H, MODE>), dim3((unsigned)grid), blk, 0, st,
                          static_cast<const uint16_t*>(src), rows, cols,

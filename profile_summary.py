@@ -8,6 +8,13 @@ min and max duration in microseconds; with ``--pmc`` it averages the
 counter columns of a ``*_counter_collection.csv`` per (kernel, grid).
 
 usage: python profile_summary.py TRACE_CSV [--pmc COUNTER_CSV]
+       python profile_summary.py --traffic FETCH_CSV WRITE_CSV KERNEL_SRC OUT_JSON
+
+--traffic turns two counter runs of `bench.py --pmc-gemm` (FETCH_SIZE, then
+WRITE_SIZE, in KiB per dispatch) into HBM bytes per GEMM launch. Each counter
+is scaled by bytes / counter of the 1 GiB copy kernel in the same run (the
+copy reads and writes exactly 2^30 bytes), and the result is written with
+the sha256 of the kernel source it was measured on.
 """
 from __future__ import annotations
 
@@ -51,12 +58,52 @@ def pmc_summary(path):
             print(f"| {k} | {g} | {c} | {len(vals)} | {sum(vals) / len(vals):.1f} |")
 
 
+def _per_kernel(path, counter):
+    out = defaultdict(list)
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter:
+                out[short(row["Kernel_Name"])].append(float(row["Counter_Value"]))
+    return out
+
+
+def traffic(fetch_csv, write_csv, kernel_src, out_json):
+    import hashlib
+    import json
+    fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _per_kernel(write_csv, "WRITE_SIZE")
+    copy_key = [k for k in fetch if "copyBuffer" in k or "copy" in k.lower()]
+    gemm_key = [k for k in fetch if "gemm" in k]
+    assert copy_key and gemm_key, (list(fetch), list(write))
+    ck, gk = copy_key[0], gemm_key[0]
+    copy_bytes = float(1 << 30)
+    f_factor = copy_bytes / (sum(fetch[ck]) / len(fetch[ck]) * 1024.0)
+    w_factor = copy_bytes / (sum(write[ck]) / len(write[ck]) * 1024.0)
+    g_fetch = sum(fetch[gk]) / len(fetch[gk]) * 1024.0 * f_factor
+    g_write = sum(write[gk]) / len(write[gk]) * 1024.0 * w_factor
+    with open(kernel_src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    rec = {"kernel": gk, "kernel_sha": sha, "bytes_per_launch": round(g_fetch + g_write),
+           "read_bytes": round(g_fetch), "write_bytes": round(g_write),
+           "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
+           "calibration": f"{ck}: 1 GiB device copy",
+           "algorithmic_bytes": {"A_nibbles": 8192 * 2048, "A_scales": 8192 * 128,
+                                 "B_nibbles": 28672 * 2048, "B_scales": 28672 * 128,
+                                 "C_fp32": 8192 * 28672 * 4}}
+    with open(out_json, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("trace", nargs="?")
     ap.add_argument("--pmc")
+    ap.add_argument("--traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL_SRC", "OUT_JSON"))
     a = ap.parse_args()
     if a.trace:
         trace_summary(a.trace)
     if a.pmc:
         pmc_summary(a.pmc)
+    if a.traffic:
+        traffic(*a.traffic)

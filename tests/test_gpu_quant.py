@@ -45,7 +45,8 @@ def heavy(rows, cols, seed):
 
 SHAPES = {
     0: [(1, 32), (3, 96), (257, 160), (64, 4128)],
-    1: [(32, 1), (64, 7), (32, 100), (96, 520), (128, 1544), (160, 8)],
+    1: [(32, 1), (64, 7), (32, 100), (96, 520), (128, 1544), (160, 8), (256, 300), (384, 4),
+        (128, 260)],
     2: [(32, 32), (64, 96), (96, 320), (32, 4096)],
 }
 
