@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
 // g(r) = ((r >> 1) ^ (r >> 3)) & 3 for 4 chunks, (r ^ (r >> 3)) & 7 for 8.
 namespace big {
 
-constexpr int GROUP_M = 8;
+constexpr int GROUP_M = 4;
 
 // Staging registers use the native vector type: HIP's uint4 is a class
 // whose copies lower to memcpy, which keeps the struct in scratch memory.
@@ -295,8 +295,38 @@ struct Cfg {
 template <class G>
 struct Offs {
   uint32_t a[G::CA], b[G::CB], s[G::SC];
-  bool s_isA[G::SC];
 };
+
+// Buffer resources of the operands. Loads go through them with a 32-bit
+// per-lane offset and the k-tile offset in a scalar register, so the
+// per-lane offsets stay 32-bit and no 64-bit address arithmetic is needed
+// per load. The record count is the operand's size: a load past it returns
+// zero instead of touching memory (the clamped offsets never get there).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)(uint32_t)bytes,
+                                           0x00020000);
+}
+
+// Scale rows d = t + NT i are rows of A for d < BM and rows of B after;
+// BM is a multiple of 64, so the choice is uniform over a wave.
+template <class G>
+struct Src {
+  rsrc_t a, b, s[G::SC];
+};
+
+template <class G>
+__device__ __forceinline__ void make_src(Src<G>& S, const uint8_t* A, const uint8_t* As,
+                                         const uint8_t* B, const uint8_t* Bs, int64_t M,
+                                         int64_t N, int64_t kbytes, int64_t kblk, int wave) {
+  S.a = make_rsrc(A, M * kbytes);
+  S.b = make_rsrc(B, N * kbytes);
+#pragma unroll
+  for (int i = 0; i < G::SC; ++i) {
+    const bool isA = 64 * wave + G::NT * i < G::BM;
+    S.s[i] = isA ? make_rsrc(As, M * kblk) : make_rsrc(Bs, N * kblk);
+  }
+}
 
 template <class G>
 __device__ __forceinline__ void make_offsets(Offs<G>& O, int64_t m0, int64_t n0, int64_t M,
@@ -311,9 +341,8 @@ __device__ __forceinline__ void make_offsets(Offs<G>& O, int64_t m0, int64_t n0,
 #pragma unroll
   for (int i = 0; i < G::SC; ++i) {
     const int d = t + G::NT * i;
-    O.s_isA[i] = d < G::BM;
-    O.s[i] = (uint32_t)(O.s_isA[i] ? min(m0 + d, M - 1) * kblk
-                                   : min(n0 + min(d - G::BM, G::BN - 1), N - 1) * kblk);
+    O.s[i] = (uint32_t)(d < G::BM ? min(m0 + d, M - 1) * kblk
+                                  : min(n0 + min(d - G::BM, G::BN - 1), N - 1) * kblk);
   }
 }
 
@@ -329,26 +358,19 @@ struct Regs {
 };
 
 template <class G>
-__device__ __forceinline__ void gload(Regs<G>& R, const Offs<G>& O, const uint8_t* __restrict__ A,
-                                      const uint8_t* __restrict__ As,
-                                      const uint8_t* __restrict__ B,
-                                      const uint8_t* __restrict__ Bs, int kt) {
+__device__ __forceinline__ void gload(Regs<G>& R, const Offs<G>& O, const Src<G>& S, int kt) {
   constexpr int KB = G::CPR * 16;
-  const uint8_t* Ak = A + (int64_t)kt * KB;
-  const uint8_t* Bk = B + (int64_t)kt * KB;
-  const uint8_t* Ask = As + (int64_t)kt * G::SB;
-  const uint8_t* Bsk = Bs + (int64_t)kt * G::SB;
+  const int ko = kt * KB, so = kt * G::SB;
 #pragma unroll
-  for (int i = 0; i < G::CA; ++i) R.a[i] = *reinterpret_cast<const u32x4*>(Ak + O.a[i]);
+  for (int i = 0; i < G::CA; ++i) R.a[i] = __builtin_amdgcn_raw_buffer_load_b128(S.a, O.a[i], ko, 0);
 #pragma unroll
-  for (int i = 0; i < G::CB; ++i) R.b[i] = *reinterpret_cast<const u32x4*>(Bk + O.b[i]);
+  for (int i = 0; i < G::CB; ++i) R.b[i] = __builtin_amdgcn_raw_buffer_load_b128(S.b, O.b[i], ko, 0);
 #pragma unroll
   for (int i = 0; i < G::SC; ++i) {
-    const uint8_t* p = (O.s_isA[i] ? Ask : Bsk) + O.s[i];
     if (G::SB == 8) {
-      R.s[i] = *reinterpret_cast<const u32x2*>(p);
+      R.s[i] = __builtin_amdgcn_raw_buffer_load_b64(S.s[i], O.s[i], so, 0);
     } else {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+      const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(S.s[i], O.s[i], so, 0);
       R.s[i] = u32x2{w, w};
     }
   }
@@ -366,7 +388,10 @@ __device__ __forceinline__ void lstore(const Regs<G>& R, uint8_t* st, int t) {
 #pragma unroll
   for (int i = 0; i < G::SC; ++i) {
     const int d = t + G::NT * i;
-    if (d < G::BM + G::BN) {
+    // When the block's threads cover the scale rows exactly the test is
+    // static: a run-time one lets the compiler sink the scale load of gload
+    // into the guarded block, right before its use, exposing its latency.
+    if (G::SC * G::NT == G::BM + G::BN || d < G::BM + G::BN) {
       if (G::SB == 8)
         *reinterpret_cast<u32x2*>(st + G::SOFF + d * 8) = R.s[i];
       else
@@ -467,21 +492,23 @@ __device__ __forceinline__ void order_after_mfma(v16f (&acc)[TN][TM]) {
 // round-robin over the 8 XCDs; the remap gives each XCD a contiguous range
 // of logical tiles, walked in groups of GROUP_M tile-rows so that the tiles
 // resident at once on one XCD share rows of A and columns of B in its L2.
+template <int GM>
 __device__ __forceinline__ void tile_of(int64_t wg, int64_t nwg, int64_t ntm, int64_t ntn,
                                         int64_t& tm, int64_t& tn) {
   const int64_t per = nwg / 8;
   int64_t lg = wg;
   if (wg < per * 8) lg = (wg % 8) * per + wg / 8;
-  const int64_t width = (int64_t)GROUP_M * ntn;
+  const int64_t width = (int64_t)GM * ntn;
   const int64_t g = lg / width;
-  const int64_t first = g * GROUP_M;
-  const int64_t gs = min(ntm - first, (int64_t)GROUP_M);
+  const int64_t first = g * GM;
+  const int64_t gs = min(ntm - first, (int64_t)GM);
   const int64_t r = lg % width;
   tm = first + r % gs;
   tn = r / gs;
 }
 
-template <int WM, int WN, int TM, int TN, int KB, int NS, int WPE, int OUT, bool VEC, int KROT = 4>
+template <int WM, int WN, int TM, int TN, int KB, int NS, int WPE, int OUT, bool VEC,
+          int GM = GROUP_M>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WM * WN, 64 * WM * WN),
                           amdgpu_waves_per_eu(WPE)))
 void gemm_big_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
@@ -494,7 +521,7 @@ void gemm_big_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   const int wm = wave / WN, wn = wave % WN;
   const int64_t ntm = (M + G::BM - 1) / G::BM, ntn = (N + G::BN - 1) / G::BN;
   int64_t tm, tn;
-  tile_of(blockIdx.x, gridDim.x, ntm, ntn, tm, tn);
+  tile_of<GM>(blockIdx.x, gridDim.x, ntm, ntn, tm, tn);
   const int64_t m0 = tm * G::BM, n0 = tn * G::BN;
   const int64_t kbytes = K / 2, kblk = K / 32;
   const int nkt = (int)(kbytes / KB);
@@ -513,25 +540,21 @@ void gemm_big_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   // (redundant) loads at the end land in a buffer nobody reads again.
   Offs<G> O;
   make_offsets<G>(O, m0, n0, M, N, kbytes, kblk, t);
-  // Each tile walks its k-tiles starting at its own offset: operand rows have
-  // a power-of-two pitch, so tiles in lockstep at the same k would all load
-  // from the same few L2 channels. (The sum order per output is fixed per
-  // tile, so results stay deterministic.)
-  const int kofs = (int)(((tm * ntn + tn) * KROT) % nkt);
-  auto kk = [&](int k) { return (k + kofs) % nkt; };
+  Src<G> S;
+  make_src<G>(S, A, As, B, Bs, M, N, kbytes, kblk, wave);
   if (NS == 2) {
     Regs<G> R0, R1;
-    gload<G>(R0, O, A, As, B, Bs, kk(0));
-    gload<G>(R1, O, A, As, B, Bs, kk(min(1, nkt - 1)));
+    gload<G>(R0, O, S, 0);
+    gload<G>(R1, O, S, min(1, nkt - 1));
     lstore<G>(R0, lds, t);
     lds_barrier();
     for (int kt = 0; kt < nkt; kt += 2) {
-      gload<G>(R0, O, A, As, B, Bs, kk(min(kt + 2, nkt - 1)));
+      gload<G>(R0, O, S, min(kt + 2, nkt - 1));
       compute<G, TM, TN>(lds, acc, arow0, brow0, lane);
       order_after_mfma<TM, TN>(acc);
       lstore<G>(R1, lds + G::STAGE, t);
       lds_barrier();
-      gload<G>(R1, O, A, As, B, Bs, kk(min(kt + 3, nkt - 1)));
+      gload<G>(R1, O, S, min(kt + 3, nkt - 1));
       compute<G, TM, TN>(lds + G::STAGE, acc, arow0, brow0, lane);
       order_after_mfma<TM, TN>(acc);
       lstore<G>(R0, lds, t);
@@ -539,16 +562,16 @@ void gemm_big_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
     }
   } else {
     Regs<G> R;
-    gload<G>(R, O, A, As, B, Bs, kk(0));
+    gload<G>(R, O, S, 0);
     lstore<G>(R, lds, t);
     lds_barrier();
     for (int kt = 0; kt < nkt; kt += 2) {
-      gload<G>(R, O, A, As, B, Bs, kk(min(kt + 1, nkt - 1)));
+      gload<G>(R, O, S, min(kt + 1, nkt - 1));
       compute<G, TM, TN>(lds, acc, arow0, brow0, lane);
       order_after_mfma<TM, TN>(acc);
       lstore<G>(R, lds + G::STAGE, t);
       lds_barrier();
-      gload<G>(R, O, A, As, B, Bs, kk(min(kt + 2, nkt - 1)));
+      gload<G>(R, O, S, min(kt + 2, nkt - 1));
       compute<G, TM, TN>(lds + G::STAGE, acc, arow0, brow0, lane);
       order_after_mfma<TM, TN>(acc);
       lstore<G>(R, lds, t);
