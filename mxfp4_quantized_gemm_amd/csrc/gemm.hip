@@ -15,17 +15,17 @@
 // E8M0 byte of that 32-block in the byte of its scale register picked by
 // op_sel. Output lane l, register r holds C[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32].
 //
-// Two kernel families. The large-tile kernels (namespace big, below) serve
-// K % 256 == 0. The general kernel here serves any K % 32 == 0 and any M, N:
-// a 256-thread work-group (4 waves, 2 x 2) computes a 128 x 128
-// tile of C; each wave a 64 x 64 sub-tile (2 x 2 MFMA tiles, 64 fp32
-// accumulators per lane). The k-loop steps 256 elements (128 bytes of
-// nibbles per row, 8 scale bytes per row). Tiles of A and B are staged in
-// LDS with a 16-byte-chunk XOR swizzle (chunk c of row r stored at c ^ (r & 7))
-// so that the 32 rows read by one ds_read_b128 hit distinct banks. LDS is
-// double-buffered: the global loads of tile k+1 are issued before the MFMAs
-// of tile k and written to the other buffer after them, with one barrier
-// per k-tile.
+// Two kernel families. The large-tile kernel (namespace lt, below) serves
+// K % 256 == 0 with 32-bit operand offsets. The general kernel here serves
+// any K % 32 == 0 and any M, N: a 256-thread work-group (4 waves, 2 x 2)
+// computes a 128 x 128 tile of C; each wave a 64 x 64 sub-tile (2 x 2 MFMA
+// tiles, 64 fp32 accumulators per lane). The k-loop steps 256 elements (128
+// bytes of nibbles per row, 8 scale bytes per row). Tiles of A and B are
+// staged in LDS with a 16-byte-chunk XOR swizzle (chunk c of row r stored at
+// c ^ (r & 7)) so that the 32 rows read by one ds_read_b128 hit distinct
+// banks. LDS is double-buffered: the global loads of tile k+1 are issued
+// before the MFMAs of tile k and written to the other buffer after them,
+// with one barrier per k-tile.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -227,16 +227,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
 }
 
 
-// ===================================================================== big
-// Large-tile kernels for K % 256 == 0 (every Llama shape), templated on the
-// wave layout: WM x WN waves per work-group, each computing TM x TN MFMA
-// 32x32x64 tiles, so the work-group tile is (32 WM TM) x (32 WN TN); on the
-// k-tile depth, KB bytes of nibbles per operand row (64 or 128, i.e. 128 or
-// 256 elements; 128 bytes reads whole cache lines); and on NS, the number of
-// k-tiles staged in registers ahead of the MFMAs (1 or 2). Global loads of
-// later k-tiles are issued into registers before the MFMAs of tile t and
-// written to the free LDS buffer after them; two LDS buffers, one LDS-only
-// barrier per k-tile, so the prefetch stays in flight across it.
+// ====================================================== large-tile kernel
+// For K % 256 == 0 (every Llama shape). Templated on the wave layout: WM x WN
+// waves per work-group, each computing TM x TN MFMA 32x32x64 tiles, so the
+// work-group tile is (32 WM TM) x (32 WN TN); and on the k-tile depth, KB
+// bytes of nibbles per operand row (64 or 128, i.e. 128 or 256 elements;
+// 128 bytes reads whole cache lines).
 //
 // Operand roles are swapped in the MFMA (B as the instruction's first
 // operand), so a lane's accumulator registers 4q..4q+3 hold four
@@ -246,8 +242,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
 // at c ^ g(r), which spreads the rows read together by one ds_read_b128
 // over distinct banks for both 8- and 16-lane service groups:
 // g(r) = ((r >> 1) ^ (r >> 3)) & 3 for 4 chunks, (r ^ (r >> 3)) & 7 for 8.
-namespace big {
+namespace lt {
 
+// Output tiles are walked in groups of GROUP_M tile-rows (see tile_of).
 constexpr int GROUP_M = 4;
 
 // Staging registers use the native vector type: HIP's uint4 is a class
@@ -271,27 +268,11 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int WM, int WN, int TM, int TN, int KB>
-struct Cfg {
-  static constexpr int NT = 64 * WM * WN;
-  static constexpr int BM = 32 * WM * TM, BN = 32 * WN * TN;
-  static constexpr int CPR = KB / 16;                    // 16-byte chunks per row
-  static constexpr int SB = KB / 16;                     // scale bytes per row per k-tile
-  static constexpr int KSTEPS = KB / 32;                 // MFMA k-steps (64 elements each)
-  static constexpr int TA = BM * KB, TB = BN * KB;
-  static constexpr int SOFF = TA + TB;                   // scales: A rows then B rows
-  static constexpr int STAGE = TA + TB + (BM + BN) * SB;
-  static constexpr int RSTEP = NT / CPR;                 // rows between a thread's chunks
-  static constexpr int CA = BM / RSTEP, CB = BN / RSTEP; // chunks per thread
-  static constexpr int SC = (BM + BN + NT - 1) / NT;     // scale rows per thread
-  static_assert(BM % RSTEP == 0 && BN % RSTEP == 0 && RSTEP % 32 == 0, "bad tiling");
-};
-
 // Per-thread global offsets (32-bit, relative to the operand base; the k-tile
 // offset is added to the uniform base): chunk c = t % CPR of rows
 // t / CPR + RSTEP i, clamped to the last row (results of clamped rows are
 // never stored), and the scale rows d = t + NT i (A rows, then B rows; a d
-// past the tile reloads a valid B row that lstore drops).
+// past the tile reloads a valid B row whose words go to a trash slot).
 template <class G>
 struct Offs {
   uint32_t a[G::CA], b[G::CB], s[G::SC];
@@ -346,11 +327,6 @@ __device__ __forceinline__ void make_offsets(Offs<G>& O, int64_t m0, int64_t n0,
   }
 }
 
-// Staging registers use the native vector type: HIP's uint4 is a class
-// whose copies lower to memcpy, which keeps the struct in scratch memory.
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
 template <class G>
 struct Regs {
   u32x4 a[G::CA], b[G::CB];
@@ -376,118 +352,6 @@ __device__ __forceinline__ void gload(Regs<G>& R, const Offs<G>& O, const Src<G>
   }
 }
 
-template <class G>
-__device__ __forceinline__ void lstore(const Regs<G>& R, uint8_t* st, int t) {
-  constexpr int KB = G::CPR * 16;
-  const int r0 = t / G::CPR, c = t % G::CPR;
-  uint8_t* pa = st + r0 * KB + ((c ^ swz<KB>(r0 & 31)) << 4);
-#pragma unroll
-  for (int i = 0; i < G::CA; ++i) *reinterpret_cast<u32x4*>(pa + i * G::RSTEP * KB) = R.a[i];
-#pragma unroll
-  for (int i = 0; i < G::CB; ++i) *reinterpret_cast<u32x4*>(pa + G::TA + i * G::RSTEP * KB) = R.b[i];
-#pragma unroll
-  for (int i = 0; i < G::SC; ++i) {
-    const int d = t + G::NT * i;
-    // When the block's threads cover the scale rows exactly the test is
-    // static: a run-time one lets the compiler sink the scale load of gload
-    // into the guarded block, right before its use, exposing its latency.
-    if (G::SC * G::NT == G::BM + G::BN || d < G::BM + G::BN) {
-      if (G::SB == 8)
-        *reinterpret_cast<u32x2*>(st + G::SOFF + d * 8) = R.s[i];
-      else
-        *reinterpret_cast<uint32_t*>(st + G::SOFF + d * 4) = R.s[i].x;
-    }
-  }
-}
-
-// One k-tile: KSTEPS k-steps of TM x TN MFMAs. The fragments of k-step s+1
-// are read from LDS while the MFMAs of k-step s run (two fragment sets);
-// scheduling barriers keep the compiler from hoisting every k-step's reads
-// at once. Lane l reads rows (row0 + 32 i + l % 32), chunk (2s + l / 32)
-// ^ swz(l % 32): one base address per k-step, tile offsets immediate.
-// Scale word of a row for k-step pair p: the row's scale bytes shifted by
-// 8 * (l / 32), so byte 2s' of the word is this lane's block for k-step
-// 2p + s'; op_sel 0 / 2 picks it.
-template <class G, int TM, int TN>
-__device__ __forceinline__ void compute(const uint8_t* st, v16f (&acc)[TN][TM], int arow0,
-                                        int brow0, int lane) {
-  constexpr int KB = G::CPR * 16;
-  const int half = lane >> 5, l32 = lane & 31;
-  const int g = swz<KB>(l32);
-  const uint8_t* pa = st + (arow0 + l32) * KB;
-  const uint8_t* pb = st + G::TA + (brow0 + l32) * KB;
-  int sa[TM][2], sb[TN][2];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const uint8_t* ps = st + G::SOFF + (arow0 + l32 + 32 * i) * G::SB;
-    if (G::SB == 8) {
-      const uint64_t v = *reinterpret_cast<const uint64_t*>(ps) >> (8 * half);
-      sa[i][0] = (int)(uint32_t)v;
-      sa[i][1] = (int)(uint32_t)(v >> 32);
-    } else {
-      sa[i][0] = (int)(*reinterpret_cast<const uint32_t*>(ps) >> (8 * half));
-      sa[i][1] = 0;
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const uint8_t* ps = st + G::SOFF + (G::BM + brow0 + l32 + 32 * j) * G::SB;
-    if (G::SB == 8) {
-      const uint64_t v = *reinterpret_cast<const uint64_t*>(ps) >> (8 * half);
-      sb[j][0] = (int)(uint32_t)v;
-      sb[j][1] = (int)(uint32_t)(v >> 32);
-    } else {
-      sb[j][0] = (int)(*reinterpret_cast<const uint32_t*>(ps) >> (8 * half));
-      sb[j][1] = 0;
-    }
-  }
-  v8i af[2][TM], bf[2][TN];
-#pragma unroll
-  for (int s = 0; s <= G::KSTEPS; ++s) {
-    if (s < G::KSTEPS) {
-      const int co = ((2 * s + half) ^ g) << 4;
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const u32x4 q = *reinterpret_cast<const u32x4*>(pa + co + i * 32 * KB);
-        af[s & 1][i] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const u32x4 q = *reinterpret_cast<const u32x4*>(pb + co + j * 32 * KB);
-        bf[s & 1][j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-      }
-    }
-    if (s > 0) {
-      const int u = s - 1, x = u & 1;
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          if ((u & 1) == 0)
-            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                bf[x][j], af[x][i], acc[j][i], 4, 4, 0, sb[j][u >> 1], 0, sa[i][u >> 1]);
-          else
-            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                bf[x][j], af[x][i], acc[j][i], 4, 4, 2, sb[j][u >> 1], 2, sa[i][u >> 1]);
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// Ordering point: every MFMA issued so far must have been issued before any
-// later memory operation. MFMAs touch no memory, so without this the
-// compiler may sink a k-tile's MFMAs below the next LDS stores and barrier,
-// which leaves the global-load latency of the prefetch uncovered. The empty
-// asm reads the accumulators (in AGPRs) and clobbers memory.
-template <int TM, int TN>
-__device__ __forceinline__ void order_after_mfma(v16f (&acc)[TN][TM]) {
-#pragma unroll
-  for (int j = 0; j < TN; ++j)
-#pragma unroll
-    for (int i = 0; i < TM; ++i) asm volatile("" ::"a"(acc[j][i]) : "memory");
-}
-
 // Work-group id -> output tile. Consecutive work-group ids are dispatched
 // round-robin over the 8 XCDs; the remap gives each XCD a contiguous range
 // of logical tiles, walked in groups of GROUP_M tile-rows so that the tiles
@@ -507,13 +371,275 @@ __device__ __forceinline__ void tile_of(int64_t wg, int64_t nwg, int64_t ntm, in
   tn = r / gs;
 }
 
-template <int WM, int WN, int TM, int TN, int KB, int NS, int WPE, int OUT, bool VEC,
-          int GM = GROUP_M>
+// Large-tile kernel, software pipelined. A 512-thread work-group (8 waves,
+// 2 x 4) computes a 256 x 256 tile of C, each wave 128 x 64 (4 x 2 MFMA
+// tiles, 128 fp32 accumulators per lane, in AGPRs). k-tiles are KB = 128
+// (256-deep) or 64 (128-deep) bytes of every operand row; A and B rows are
+// staged in LDS as rows of KB bytes with a lane-constant 16-byte-chunk
+// swizzle, double-buffered, loaded through buffer resources into staging
+// registers. Within a k-tile:
+//  * scale bytes are stored in LDS pre-split into an "even blocks" word and
+//    an "odd blocks" word per row, laid out so that a lane's TM (TN) rows are
+//    consecutive: one vector LDS read per operand per k-tile, and byte s of
+//    the lane's word is its block for k-step s, so op_sel is the k-step;
+//  * the fragment reads of k-step s+1, the LDS writes of the next k-tile and
+//    the global loads of a later k-tile are interleaved one by one with the
+//    MFMAs of k-step s (scheduling groups), instead of being left to the
+//    scheduler, which bunches the reads behind the MFMAs;
+//  * the barrier comes before the last k-step: its MFMAs (operands already
+//    in registers) are issued after it, together with the first reads of the
+//    next k-tile, so neither the barrier nor that read latency idles the
+//    matrix cores;
+//  * the next k-tile's staging registers are written to LDS early in the
+//    k-tile (the other LDS buffer is free once the previous barrier passed),
+//    then reloaded with a later k-tile (NS = 2 staging sets would run the
+//    loads two k-tiles ahead; the 8-wave shape has registers for one).
+template <int WM, int WN, int TM, int TN, int KB>
+struct Cfg {
+  static constexpr int NT = 64 * WM * WN;
+  static constexpr int BM = 32 * WM * TM, BN = 32 * WN * TN;
+  static constexpr int CPR = KB / 16;                    // 16-byte chunks per row
+  static constexpr int SB = KB / 16;                     // scale bytes per row per k-tile
+  static constexpr int KSTEPS = KB / 32;                 // MFMA k-steps (64 elements each)
+  static constexpr int TA = BM * KB, TB = BN * KB;
+  static constexpr int SOFF = TA + TB;                   // A scale words, then B scale words
+  static constexpr int SBOFF = SOFF + BM * 8;
+  static constexpr int TRASH = SBOFF + BN * 8;           // sink for surplus scale rows
+  static constexpr int STAGE = TRASH + 16;
+  static constexpr int RSTEP = NT / CPR;                 // rows between a thread's chunks
+  static constexpr int CA = BM / RSTEP, CB = BN / RSTEP; // chunks per thread
+  static constexpr int SC = (BM + BN + NT - 1) / NT;     // scale rows per thread
+  static_assert(BM % RSTEP == 0 && BN % RSTEP == 0 && RSTEP % 32 == 0, "bad tiling");
+  static_assert(KB == 64 || KB == 128, "k-tiles of 128 or 256 elements");
+};
+
+// LDS byte offsets (within a stage) of the even and odd scale words of the
+// thread's scale rows. Row r = 32 (T g + i) + l of the A tile (T = TM rows
+// per wave row g) goes to word ((32 g + l) 2 + h) T + i for parity h, so the
+// lane (l, h) of wave row g finds its T words side by side; B likewise after
+// the A words.
+template <class G, int TM, int TN>
+struct SPos {
+  uint32_t e[G::SC], o[G::SC];
+};
+
+template <class G, int TM, int TN>
+__device__ __forceinline__ void make_spos(SPos<G, TM, TN>& P, int t) {
+#pragma unroll
+  for (int i = 0; i < G::SC; ++i) {
+    const int d = t + G::NT * i;
+    if (d >= G::BM + G::BN) {
+      // No row: the (redundant, clamped) load of this slot is written to the
+      // trash words, so loads and stores stay unconditional.
+      P.e[i] = P.o[i] = G::TRASH;
+    } else if (d < G::BM) {
+      const int g = d / (32 * TM), ii = (d / 32) % TM, l = d % 32;
+      P.e[i] = G::SOFF + 4 * ((g * 32 + l) * 2 * TM + ii);
+      P.o[i] = P.e[i] + 4 * TM;
+    } else {
+      const int e = d - G::BM;
+      const int g = e / (32 * TN), jj = (e / 32) % TN, l = e % 32;
+      P.e[i] = G::SBOFF + 4 * ((g * 32 + l) * 2 * TN + jj);
+      P.o[i] = P.e[i] + 4 * TN;
+    }
+  }
+}
+
+// Part P of NP of the staging registers -> LDS stage st (chunks in the
+// swizzled row layout; the scale words go with the last part).
+template <class G, int TM, int TN, int P, int NP>
+__device__ __forceinline__ void lstore_part(const Regs<G>& R, const SPos<G, TM, TN>& SP,
+                                            uint8_t* st, int t) {
+  constexpr int KB = G::CPR * 16;
+  const int r0 = t / G::CPR, c = t % G::CPR;
+  uint8_t* pa = st + r0 * KB + ((c ^ swz<KB>(r0 & 31)) << 4);
+#pragma unroll
+  for (int i = G::CA * P / NP; i < G::CA * (P + 1) / NP; ++i)
+    *reinterpret_cast<u32x4*>(pa + i * G::RSTEP * KB) = R.a[i];
+#pragma unroll
+  for (int i = G::CB * P / NP; i < G::CB * (P + 1) / NP; ++i)
+    *reinterpret_cast<u32x4*>(pa + G::TA + i * G::RSTEP * KB) = R.b[i];
+  if (P == NP - 1) {
+#pragma unroll
+    for (int i = 0; i < G::SC; ++i) {
+      const uint32_t lo = R.s[i].x, hi = R.s[i].y;
+      uint32_t ev, od;
+      if (G::SB == 8) {
+        ev = (lo & 0xffu) | ((lo >> 8) & 0xff00u) | ((hi & 0xffu) << 16) | ((hi << 8) & 0xff000000u);
+        od = ((lo >> 8) & 0xffu) | ((lo >> 16) & 0xff00u) | (((hi >> 8) & 0xffu) << 16) |
+             (hi & 0xff000000u);
+      } else {
+        ev = (lo & 0xffu) | ((lo >> 8) & 0xff00u);
+        od = ((lo >> 8) & 0xffu) | ((lo >> 16) & 0xff00u);
+      }
+      *reinterpret_cast<uint32_t*>(st + SP.e[i]) = ev;
+      *reinterpret_cast<uint32_t*>(st + SP.o[i]) = od;
+    }
+  }
+}
+
+template <int T>
+__device__ __forceinline__ void lds_words(const uint8_t* p, int (&w)[T]) {
+  if constexpr (T == 4) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(p);
+    w[0] = (int)q.x; w[1] = (int)q.y; w[2] = (int)q.z; w[3] = (int)q.w;
+  } else if constexpr (T == 2) {
+    const u32x2 q = *reinterpret_cast<const u32x2*>(p);
+    w[0] = (int)q.x; w[1] = (int)q.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < T; ++i) w[i] = *reinterpret_cast<const int*>(p + 4 * i);
+  }
+}
+
+template <int TM, int TN>
+struct Frag {
+  v8i a[TM], b[TN];
+};
+
+template <int TM, int TN>
+struct Scl {
+  int a[TM], b[TN];
+};
+
+// Per-lane LDS read addresses, relative to a stage.
+struct RAddr {
+  uint32_t fa, fb, sa, sb;
+  int g, half;
+};
+
+template <class G, int TM, int TN>
+__device__ __forceinline__ RAddr make_raddr(int wm, int wn, int lane) {
+  constexpr int KB = G::CPR * 16;
+  RAddr r;
+  const int l32 = lane & 31;
+  r.half = lane >> 5;
+  r.g = swz<KB>(l32);
+  r.fa = (uint32_t)((wm * TM * 32 + l32) * KB);
+  r.fb = (uint32_t)(G::TA + (wn * TN * 32 + l32) * KB);
+  r.sa = (uint32_t)(G::SOFF + 4 * ((wm * 32 + l32) * 2 + r.half) * TM);
+  r.sb = (uint32_t)(G::SBOFF + 4 * ((wn * 32 + l32) * 2 + r.half) * TN);
+  return r;
+}
+
+template <class G, int TM, int TN, int S>
+__device__ __forceinline__ void read_frags(const uint8_t* st, const RAddr& ra, Frag<TM, TN>& F) {
+  constexpr int KB = G::CPR * 16;
+  const int co = ((2 * S + ra.half) ^ ra.g) << 4;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(st + ra.fa + co + i * 32 * KB);
+    F.a[i] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(st + ra.fb + co + j * 32 * KB);
+    F.b[j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+  }
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void read_scales(const uint8_t* st, const RAddr& ra, Scl<TM, TN>& S) {
+  lds_words<TM>(st + ra.sa, S.a);
+  lds_words<TN>(st + ra.sb, S.b);
+}
+
+// MFMAs of k-step S. Operand roles are swapped (B fragment first) so that
+// accumulator register 4q + e of a lane holds four consecutive C columns.
+template <int TM, int TN, int S>
+__device__ __forceinline__ void mfma_step(const Frag<TM, TN>& F, const Scl<TM, TN>& sc,
+                                          v16f (&acc)[TN][TM]) {
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[j], F.a[i], acc[j][i], 4, 4,
+                                                                  S, sc.b[j], S, sc.a[i]);
+}
+
+// Scheduling groups for one k-step: NM MFMAs, each followed by its share of
+// NR LDS reads (front-loaded, one per MFMA), NW LDS writes and NL global loads
+// (spread evenly).
+template <int R, int NM, int NR, int NW, int NL>
+__device__ __forceinline__ void interleave() {
+  if constexpr (R < NM) {
+    constexpr int r = (R < NR) ? ((R == NM - 1) ? NR - R : 1) : 0;
+    constexpr int w = NW * (R + 1) / NM - NW * R / NM;
+    constexpr int l = NL * (R + 1) / NM - NL * R / NM;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+    if constexpr (w > 0) __builtin_amdgcn_sched_group_barrier(0x200, w, 0);
+    if constexpr (l > 0) __builtin_amdgcn_sched_group_barrier(0x020, l, 0);
+    interleave<R + 1, NM, NR, NW, NL>();
+  }
+}
+
+template <class G, int TM, int TN, int NS>
+struct Pipe {
+  static constexpr int NM = TM * TN, NR = TM + TN;
+  static constexpr int NWR = G::CA + G::CB + 2 * G::SC;   // LDS writes per k-tile
+  static constexpr int NLD = G::CA + G::CB + G::SC;       // global loads per k-tile
+};
+
+// One k-tile (stage C holds it; F0 / SCc hold its k-step-0 fragments and its
+// scales). Leaves the next k-tile's k-step-0 fragments in F0 and its scales in
+// SCn, the next k-tile written to stage C ^ 1, and tile k + 1 + NS loading
+// into the staging set just written.
+template <class G, int TM, int TN, int NS, int C>
+__device__ __forceinline__ void ktile(uint8_t* lds, const RAddr& ra, Regs<G> (&R)[NS],
+                                      const SPos<G, TM, TN>& SP, const Offs<G>& O,
+                                      const Src<G>& S, Frag<TM, TN>& F0, Frag<TM, TN>& F1,
+                                      const Scl<TM, TN>& SCc, Scl<TM, TN>& SCn,
+                                      v16f (&acc)[TN][TM], int k, int nkt, int t) {
+  using PP = Pipe<G, TM, TN, NS>;
+  uint8_t* cur = lds + C * G::STAGE;
+  uint8_t* nxt = lds + (C ^ 1) * G::STAGE;
+  constexpr int X = (NS == 1) ? 0 : (C ^ 1);  // staging set holding tile k + 1
+  const int kl = min(k + 1 + NS, nkt - 1);
+  if constexpr (G::KSTEPS == 4) {
+    read_frags<G, TM, TN, 1>(cur, ra, F1);
+    lstore_part<G, TM, TN, 0, 2>(R[X], SP, nxt, t);
+    mfma_step<TM, TN, 0>(F0, SCc, acc);
+    interleave<0, PP::NM, PP::NR, (G::CA + G::CB) / 2, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags<G, TM, TN, 2>(cur, ra, F0);
+    lstore_part<G, TM, TN, 1, 2>(R[X], SP, nxt, t);
+    gload<G>(R[X], O, S, kl);
+    mfma_step<TM, TN, 1>(F1, SCc, acc);
+    interleave<0, PP::NM, PP::NR, PP::NWR - (G::CA + G::CB) / 2, PP::NLD>();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags<G, TM, TN, 3>(cur, ra, F1);
+    mfma_step<TM, TN, 2>(F0, SCc, acc);
+    interleave<0, PP::NM, PP::NR, 0, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    read_scales<TM, TN>(nxt, ra, SCn);
+    read_frags<G, TM, TN, 0>(nxt, ra, F0);
+    mfma_step<TM, TN, 3>(F1, SCc, acc);
+    interleave<0, PP::NM, PP::NR + 2, 0, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    read_frags<G, TM, TN, 1>(cur, ra, F1);
+    lstore_part<G, TM, TN, 0, 1>(R[X], SP, nxt, t);
+    gload<G>(R[X], O, S, kl);
+    mfma_step<TM, TN, 0>(F0, SCc, acc);
+    interleave<0, PP::NM, PP::NR, PP::NWR, PP::NLD>();
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    read_scales<TM, TN>(nxt, ra, SCn);
+    read_frags<G, TM, TN, 0>(nxt, ra, F0);
+    mfma_step<TM, TN, 1>(F1, SCc, acc);
+    interleave<0, PP::NM, PP::NR + 2, 0, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int WM, int WN, int TM, int TN, int KB, int NS, int WPE, int OUT, bool VEC>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WM * WN, 64 * WM * WN),
                           amdgpu_waves_per_eu(WPE)))
-void gemm_big_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
-                     const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, int64_t M,
-                     int64_t N, int64_t K, void* __restrict__ C) {
+void gemm_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
+                      const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, int64_t M,
+                      int64_t N, int64_t K, void* __restrict__ C) {
   using G = Cfg<WM, WN, TM, TN, KB>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * G::STAGE];
   const int t = threadIdx.x, lane = t & 63;
@@ -521,7 +647,7 @@ void gemm_big_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   const int wm = wave / WN, wn = wave % WN;
   const int64_t ntm = (M + G::BM - 1) / G::BM, ntn = (N + G::BN - 1) / G::BN;
   int64_t tm, tn;
-  tile_of<GM>(blockIdx.x, gridDim.x, ntm, ntn, tm, tn);
+  tile_of<GROUP_M>(blockIdx.x, gridDim.x, ntm, ntn, tm, tn);
   const int64_t m0 = tm * G::BM, n0 = tn * G::BN;
   const int64_t kbytes = K / 2, kblk = K / 32;
   const int nkt = (int)(kbytes / KB);
@@ -535,50 +661,32 @@ void gemm_big_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
 
-  // Buffer 0 holds even k-tiles, buffer 1 odd ones. Prefetch indices are
-  // clamped to the last tile so the loop body is branch-free; the clamped
-  // (redundant) loads at the end land in a buffer nobody reads again.
   Offs<G> O;
   make_offsets<G>(O, m0, n0, M, N, kbytes, kblk, t);
   Src<G> S;
   make_src<G>(S, A, As, B, Bs, M, N, kbytes, kblk, wave);
-  if (NS == 2) {
-    Regs<G> R0, R1;
-    gload<G>(R0, O, S, 0);
-    gload<G>(R1, O, S, min(1, nkt - 1));
-    lstore<G>(R0, lds, t);
-    lds_barrier();
-    for (int kt = 0; kt < nkt; kt += 2) {
-      gload<G>(R0, O, S, min(kt + 2, nkt - 1));
-      compute<G, TM, TN>(lds, acc, arow0, brow0, lane);
-      order_after_mfma<TM, TN>(acc);
-      lstore<G>(R1, lds + G::STAGE, t);
-      lds_barrier();
-      gload<G>(R1, O, S, min(kt + 3, nkt - 1));
-      compute<G, TM, TN>(lds + G::STAGE, acc, arow0, brow0, lane);
-      order_after_mfma<TM, TN>(acc);
-      lstore<G>(R0, lds, t);
-      lds_barrier();
-    }
-  } else {
-    Regs<G> R;
-    gload<G>(R, O, S, 0);
-    lstore<G>(R, lds, t);
-    lds_barrier();
-    for (int kt = 0; kt < nkt; kt += 2) {
-      gload<G>(R, O, S, min(kt + 1, nkt - 1));
-      compute<G, TM, TN>(lds, acc, arow0, brow0, lane);
-      order_after_mfma<TM, TN>(acc);
-      lstore<G>(R, lds + G::STAGE, t);
-      lds_barrier();
-      gload<G>(R, O, S, min(kt + 2, nkt - 1));
-      compute<G, TM, TN>(lds + G::STAGE, acc, arow0, brow0, lane);
-      order_after_mfma<TM, TN>(acc);
-      lstore<G>(R, lds, t);
-      lds_barrier();
-    }
-  }
+  SPos<G, TM, TN> SP;
+  make_spos<G, TM, TN>(SP, t);
+  const RAddr ra = make_raddr<G, TM, TN>(wm, wn, lane);
 
+  // Prologue: k-tile 0 into stage 0; the staging sets then hold k-tiles
+  // 1 .. NS (prefetch indices clamp to the last k-tile; the redundant loads
+  // at the end land in a stage nobody reads again).
+  Regs<G> R[NS];
+  gload<G>(R[0], O, S, 0);
+  if constexpr (NS == 2) gload<G>(R[1], O, S, min(1, nkt - 1));
+  lstore_part<G, TM, TN, 0, 1>(R[0], SP, lds, t);
+  gload<G>(R[0], O, S, min(NS == 1 ? 1 : 2, nkt - 1));
+  lds_barrier();
+  Frag<TM, TN> F0, F1;
+  Scl<TM, TN> SCa, SCb;
+  read_scales<TM, TN>(lds, ra, SCa);
+  read_frags<G, TM, TN, 0>(lds, ra, F0);
+
+  for (int k = 0; k < nkt; k += 2) {
+    ktile<G, TM, TN, NS, 0>(lds, ra, R, SP, O, S, F0, F1, SCa, SCb, acc, k, nkt, t);
+    ktile<G, TM, TN, NS, 1>(lds, ra, R, SP, O, S, F0, F1, SCb, SCa, acc, k + 1, nkt, t);
+  }
   // Epilogue: acc[j][i] register 4q + e holds C[m][n] with
   // m = m0 + arow0 + 32 i + (lane & 31), n = n0 + brow0 + 32 j + 8 q + 4 (lane >> 5) + e.
   const int half = lane >> 5, l32 = lane & 31;
@@ -632,7 +740,6 @@ void gemm_big_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   }
 }
 
-// K must be a multiple of 2 * KB * 2 (an even number of k-tiles).
 template <int WM, int WN, int TM, int TN, int KB, int NS, int WPE>
 hipError_t launch(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
                   int64_t M, int64_t N, int64_t K, void* C, int out_dtype, hipStream_t stream) {
@@ -642,23 +749,23 @@ hipError_t launch(const uint8_t* a, const uint8_t* as, const uint8_t* b, const u
   const dim3 grid((unsigned)tiles), blk(G::NT);
   if (out_dtype == 0) {
     if (vec)
-      hipLaunchKernelGGL((gemm_big_kernel<WM, WN, TM, TN, KB, NS, WPE, 0, true>), grid, blk, 0,
+      hipLaunchKernelGGL((gemm_pipe_kernel<WM, WN, TM, TN, KB, NS, WPE, 0, true>), grid, blk, 0,
                          stream, a, as, b, bs, M, N, K, C);
     else
-      hipLaunchKernelGGL((gemm_big_kernel<WM, WN, TM, TN, KB, NS, WPE, 0, false>), grid, blk, 0,
+      hipLaunchKernelGGL((gemm_pipe_kernel<WM, WN, TM, TN, KB, NS, WPE, 0, false>), grid, blk, 0,
                          stream, a, as, b, bs, M, N, K, C);
   } else {
     if (vec)
-      hipLaunchKernelGGL((gemm_big_kernel<WM, WN, TM, TN, KB, NS, WPE, 1, true>), grid, blk, 0,
+      hipLaunchKernelGGL((gemm_pipe_kernel<WM, WN, TM, TN, KB, NS, WPE, 1, true>), grid, blk, 0,
                          stream, a, as, b, bs, M, N, K, C);
     else
-      hipLaunchKernelGGL((gemm_big_kernel<WM, WN, TM, TN, KB, NS, WPE, 1, false>), grid, blk, 0,
+      hipLaunchKernelGGL((gemm_pipe_kernel<WM, WN, TM, TN, KB, NS, WPE, 1, false>), grid, blk, 0,
                          stream, a, as, b, bs, M, N, K, C);
   }
   return hipGetLastError();
 }
 
-}  // namespace big
+}  // namespace lt
 
 }  // namespace
 
@@ -670,16 +777,15 @@ hipError_t launch_gemm(const void* Aq, const void* As, const void* Bq, const voi
   const auto* bs = static_cast<const uint8_t*>(Bs);
   const dim3 blk(256);
   // Large-tile paths (the main loop runs k-tiles in pairs, so K must hold
-  // an even number of them; 32-bit per-lane operand offsets):
-  //  K % 512 == 0: 256 x 256 tile, 8 waves of 128 x 64, 256-deep k-tiles
-  //                (whole 128-byte operand rows per k-tile);
-  //  K % 256 == 0: 256 x 256 tile, 4 waves of 128 x 128, 128-deep k-tiles.
+  // an even number of them; 32-bit per-lane operand offsets): 256 x 256
+  // tiles, 8 waves of 128 x 64, with 256-deep k-tiles when K % 512 == 0 and
+  // 128-deep ones when only K % 256 == 0.
   const bool off32 = (M * (K / 2) < (int64_t(1) << 32)) && (N * (K / 2) < (int64_t(1) << 32));
   const bool sc_al = ((uintptr_t)As % 8 == 0) && ((uintptr_t)Bs % 8 == 0);
   if (off32 && sc_al && K % 512 == 0)
-    return big::launch<2, 4, 4, 2, 128, 1, 2>(a, as, b, bs, M, N, K, C, out_dtype, stream);
+    return lt::launch<2, 4, 4, 2, 128, 1, 2>(a, as, b, bs, M, N, K, C, out_dtype, stream);
   if (off32 && sc_al && K % 256 == 0)
-    return big::launch<2, 2, 4, 4, 64, 2, 1>(a, as, b, bs, M, N, K, C, out_dtype, stream);
+    return lt::launch<2, 4, 4, 2, 64, 1, 2>(a, as, b, bs, M, N, K, C, out_dtype, stream);
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const bool svec = (K % 256 == 0) && ((uintptr_t)As % 8 == 0) && ((uintptr_t)Bs % 8 == 0);
   const dim3 grid((unsigned)tiles);
