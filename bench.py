@@ -12,16 +12,23 @@ A, quantize B, MXFP4 GEMM) through the C ABI, on one stream:
 
 H16 rotation along each reduction axis, OCP-floor scales, fp32 output.
 Inputs are seeded synthetic tensors (synthetic.make) already resident in
-HBM when the timed region starts. HIP events bracket every launch in the
-timed region, giving per-kernel average durations; `value` is the step's
-total 2MNK over its wall time. The fused entry points are timed as well
-(same kernels, no inner events) as a cross-check.
+HBM when the timed region starts. The timed region is K steps launched
+back to back with nothing else on the stream; `value` is the step's total
+2MNK over its wall time. A second pass of K steps brackets every launch
+with HIP events on the launch stream, giving per-kernel average durations
+(the roofline figure). The fused entry points are timed as well (same
+kernels) as a cross-check.
 
 Also measured: the quantizer-only workload (8192 x 4096, Student-t x
 log-normal) for every axis and scale rule with H16, plus H0/H32 row-wise,
 cycling six buffer sets (> 400 MB) so the 256 MB last-level cache cannot
-hold the data, reported in GB/s of algorithmic bytes (2 B read + 0.5 B
-nibbles + 1/32 B scale per element).
+hold the data, in GB/s of algorithmic bytes (2 B read + 0.5 B nibbles +
+1/32 B scale per element): 10 warm-up launches, then 50 launches each
+bracketed by events (median, min) and 50 launched back to back between two
+events (mean, the headline GB/s); a 1 GiB device-to-device copy gives the
+achievable-HBM reference. The quantization error of every product against
+the exact product of its bf16 operands (fp64, on a row sample) is reported
+for H0/H16/H32 x both scale rules.
 
 The CPU baseline is the oracle (numpy, fp64 GEMM) timed on this host on a
 bounded sample of the same step.
@@ -86,7 +93,7 @@ def load_traffic(kernel_src):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(work, budget_rows=1024, budget_cols=4096):
+def cpu_baseline(work, budget_rows=2048, budget_cols=8192):
     """Oracle on a bounded sample of the step: for each product, a
     budget_rows x budget_cols tile of the output at full reduction length
     (quantize the matching source slices, dequantize, fp64 GEMM + sum|a||b|)."""
@@ -122,6 +129,41 @@ def cpu_baseline(work, budget_rows=1024, budget_cols=4096):
                       f"dequantize, fp64 GEMM and sum|a||b| (numpy; BLAS threads = {cores})"}
 
 
+def error_report(mx, torch, prods, stream, dev, rows=128):
+    """Quantization error of each product's fused entry point against the
+    exact product of its original bf16 operands (fp64 on the GPU, first
+    `rows` output rows), for H in {0, 16, 32} x {ocp_floor, ceil}: MSE,
+    cosine, relative Frobenius error and SNR in dB."""
+    import numpy as np
+    out = {}
+    for p in prods:
+        fn = {"fprop": mx.mxfp4_fprop, "dgrad": mx.mxfp4_dgrad, "wgrad": mx.mxfp4_wgrad}[p["op"]]
+        P64, Q64 = p["P"], p["Q"]
+        if p["op"] == "fprop":
+            ref = P64[:rows].double() @ Q64.double().t()
+        elif p["op"] == "dgrad":
+            ref = P64[:rows].double() @ Q64.double()
+        else:
+            ref = P64[:, :rows].double().t() @ Q64.double()
+        rec = {}
+        for h in (0, 16, 32):
+            for m in (0, 1):
+                fn(p["P"], p["Q"], p["T"], p["N"], p["K"], h, m, p["ws"], p["C"], mx.OUT_F32,
+                   stream)
+                c = p["C"][:rows].double()
+                d = c - ref
+                nd, nr = float((d * d).sum()), float((ref * ref).sum())
+                rec[f"h{h}_{['ocp_floor', 'ceil'][m]}"] = {
+                    "mse": float((d * d).mean()),
+                    "cosine": float((c * ref).sum() / (c.norm() * ref.norm())),
+                    "rel_fro": (nd / nr) ** 0.5,
+                    "snr_db": 10.0 * np.log10(nr / nd)}
+        out[p["name"]] = rec
+        del ref
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,15 +171,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true")
-    ap.add_argument("--quant-iters", type=int, default=30)
+    ap.add_argument("--quant-iters", type=int, default=50)
+    ap.add_argument("--no-error-report", action="store_true")
     ap.add_argument("--pmc-gemm", action="store_true",
                     help="counter-collection mode: run only the gate+up GEMM (3 launches) and a "
                          "1 GiB device-to-device copy (3 launches, the calibration kernel)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the path has no multi-GPU component; see the sharding note in the design doc)",
-              file=sys.stderr)
+              f"(the path has no multi-GPU component)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -220,26 +262,33 @@ def main():
 
     # ---------------------------------------------------------- timed region
     K_ = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)] for _ in range(K_)]
+    e_t0, e_t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    e_t0.record(stream)
+    for s in range(K_):
+        for _, _, fn in seq:
+            fn()
+    e_t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / K_
+    event_ms_per_step = e_t0.elapsed_time(e_t1) / K_
+    total_flops = sum(2.0 * p["GM"] * p["GN"] * p["GK"] for p in prods)
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+
+    # ------------------------------------- per-kernel pass (events per launch)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)] for _ in range(K_)]
     for s in range(K_):
         ev[s][0].record(stream)
         for i, (_, _, fn) in enumerate(seq):
             fn()
             ev[s][i + 1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
     kernel_ms = np.zeros(len(seq))
-    step_ms = []
     for s in range(K_):
-        d = [ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(len(seq))]
-        kernel_ms += np.array(d)
-        step_ms.append(ev[s][0].elapsed_time(ev[s][-1]))
+        kernel_ms += np.array([ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(len(seq))])
     kernel_ms /= K_
-    ms_per_step = wall * 1e3 / K_
-    total_flops = sum(2.0 * p["GM"] * p["GN"] * p["GK"] for p in prods)
-    value = total_flops / (ms_per_step * 1e-3) / 1e12
 
     per_product = {}
     kernels = []
@@ -293,33 +342,65 @@ def main():
         R, Cc = A.shape
         quant = {}
         arms = [(ax, 16, m) for ax in (0, 1, 2) for m in (0, 1)] + [(0, 0, 0), (0, 32, 0)]
+        its = args.quant_iters
         for ax, h, m in arms:
             ns_, ss_ = mx.packed_shapes(R, Cc, ax)
             outs = [(torch.empty(ns_, dtype=torch.uint8, device=dev),
                      torch.empty(ss_, dtype=torch.uint8, device=dev)) for _ in range(nsets)]
-            for i in range(nsets):
-                mx.mxfp4_quantize(srcs[i], R, Cc, ax, h, m, outs[i][0], outs[i][1], stream)
+
+            def q(i):
+                k = i % nsets
+                mx.mxfp4_quantize(srcs[k], R, Cc, ax, h, m, outs[k][0], outs[k][1], stream)
+            for i in range(10):
+                q(i)
             torch.cuda.synchronize()
-            its = args.quant_iters
             evs = [torch.cuda.Event(enable_timing=True) for _ in range(its + 1)]
             evs[0].record(stream)
             for i in range(its):
-                k = i % nsets
-                mx.mxfp4_quantize(srcs[k], R, Cc, ax, h, m, outs[k][0], outs[k][1], stream)
+                q(i)
                 evs[i + 1].record(stream)
             torch.cuda.synchronize()
             d = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(its)])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(its):
+                q(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            mean_ms = e0.elapsed_time(e1) / its
             b = quant_bytes(R, Cc, ax)
             key = f"{['row', 'col', '2d'][ax]}_h{h}_{['ocp_floor', 'ceil'][m]}"
-            quant[key] = {"us_median": round(float(np.median(d)) * 1e3, 2),
-                          "GB/s": round(b / (np.median(d) * 1e-3) / 1e9, 1),
-                          "GB/s_best": round(b / (d.min() * 1e-3) / 1e9, 1)}
+            quant[key] = {"us": round(mean_ms * 1e3, 2),
+                          "GB/s": round(b / (mean_ms * 1e-3) / 1e9, 1),
+                          "us_event_median": round(float(np.median(d)) * 1e3, 2),
+                          "us_event_min": round(float(d.min()) * 1e3, 2),
+                          "GB/s_event_median": round(b / (np.median(d) * 1e-3) / 1e9, 1)}
             quant[key]["frac_hbm"] = round(quant[key]["GB/s"] / HBM_PEAK_GBS, 4)
             del outs
         if "row_h16_ocp_floor" in quant and "row_h32_ocp_floor" in quant:
             quant["h16_over_h32_row"] = round(quant["row_h16_ocp_floor"]["GB/s"] /
                                               quant["row_h32_ocp_floor"]["GB/s"], 3)
+        # achievable-HBM reference: 1 GiB device-to-device copy (read + write)
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        quant["hbm_copy_GB/s"] = round(2 * (1 << 30) * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        del src, dst
         log("quantizer arms done")
+
+    # ------------------------------------------------------- error report
+    errs = None
+    if not args.no_error_report:
+        errs = error_report(mx, torch, prods, stream, dev)
+        log("error report done")
 
     # -------------------------------------------------------------- roofline
     dom = [k for k in kernels if k["kernel"] == f"{DOMINANT}.gemm"][0]
@@ -346,11 +427,12 @@ def main():
                                "32x1 col blocks, ocp_floor scales, fp32 out",
                    "hadamard": 16, "scale_mode": "ocp_floor", "out_dtype": "f32",
                    "parallelism": "single-gpu"},
+        "event_ms_per_step": round(event_ms_per_step, 4),
         "fused_entry_ms_per_step": round(fused_ms, 4),
-        "event_step_ms_median": round(float(np.median(step_ms)), 4),
         "products": per_product,
         "kernels": kernels,
         "quantizer": quant,
+        "error_report": errs,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
