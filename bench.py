@@ -377,6 +377,33 @@ def main():
                           "GB/s_event_median": round(b / (np.median(d) * 1e-3) / 1e9, 1)}
             quant[key]["frac_hbm"] = round(quant[key]["GB/s"] / HBM_PEAK_GBS, 4)
             del outs
+        # dual orientation: one read, row-wise + column-wise transposed outputs
+        for m in (0, 1):
+            (rn_, rs_), (cn_, cs_) = mx.packed_shapes(R, Cc, 0), mx.packed_shapes(R, Cc, 1)
+            outs = [[torch.empty(sh, dtype=torch.uint8, device=dev) for sh in (rn_, rs_, cn_, cs_)]
+                    for _ in range(nsets)]
+
+            def qd(i):
+                k = i % nsets
+                mx.mxfp4_quantize_dual(srcs[k], R, Cc, 16, m, *outs[k], stream=stream)
+            for i in range(10):
+                qd(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(its):
+                qd(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            mean_ms = e0.elapsed_time(e1) / its
+            b = R * Cc * (2 + 2 * (0.5 + 1 / 32))
+            key = f"dual_h16_{['ocp_floor', 'ceil'][m]}"
+            quant[key] = {"us": round(mean_ms * 1e3, 2), "GB/s": round(b / (mean_ms * 1e-3) / 1e9, 1),
+                          "frac_hbm": round(b / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            if f"row_h16_{['ocp_floor', 'ceil'][m]}" in quant:
+                quant[key]["speedup_vs_row_plus_col"] = round(
+                    (quant[f"row_h16_{['ocp_floor', 'ceil'][m]}"]["us"] +
+                     quant[f"col_h16_{['ocp_floor', 'ceil'][m]}"]["us"]) / (mean_ms * 1e3), 3)
+            del outs
         if "row_h16_ocp_floor" in quant and "row_h32_ocp_floor" in quant:
             quant["h16_over_h32_row"] = round(quant["row_h16_ocp_floor"]["GB/s"] /
                                               quant["row_h32_ocp_floor"]["GB/s"], 3)

@@ -105,6 +105,27 @@ int mxfp4_quantize(const void* src_bf16, int64_t rows, int64_t cols, int axis,
                    hipStream_t stream);
 
 /*
+ * mxfp4_quantize_dual -- one read of src[rows][cols], both orientations.
+ * ([P1] A.2 and D: the activation X feeds Fprop rotated and blocked along
+ * its feature axis and Wgrad rotated and blocked along the token axis;
+ * [P1] C.1 and C.3.)
+ *
+ * Writes exactly what two mxfp4_quantize calls with the same hadamard and
+ * scale_mode would write: the row-wise operand (MXFP4_AXIS_ROW) into
+ * row_nibbles [rows][cols/2] and row_e8m0 [rows][cols/32], and the
+ * column-wise transposed operand (MXFP4_AXIS_COL) into col_nibbles
+ * [cols][rows/2] and col_e8m0 [cols][rows/32]. Each output is rotated along
+ * its own blocking axis. rows % 32 == 0 and cols % 32 == 0. When
+ * rows % 128 == 0, cols % 256 == 0, row_e8m0 is 8-byte and col_e8m0 4-byte
+ * aligned, one kernel reads src once (2 B per element instead of 4);
+ * otherwise the two single-orientation kernels run back to back. Errors,
+ * alignment and empty shapes as mxfp4_quantize (both checks apply).
+ */
+int mxfp4_quantize_dual(const void* src_bf16, int64_t rows, int64_t cols,
+                        int hadamard, int scale_mode, void* row_nibbles, void* row_e8m0,
+                        void* col_nibbles, void* col_e8m0, hipStream_t stream);
+
+/*
  * mxfp4_gemm -- C[M][N] = sum_k deqA[m][k] * deqB[n][k] on gfx950's
  * block-scaled FP4 MFMA with FP32 accumulation ([P1] A.2; [P3]).
  *

@@ -23,7 +23,7 @@ OP_FPROP, OP_DGRAD, OP_WGRAD = 0, 1, 2
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp4.so")
 
 EXPORTS = (
-    "mxfp4_quantize", "mxfp4_gemm", "mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad",
+    "mxfp4_quantize", "mxfp4_quantize_dual", "mxfp4_gemm", "mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad",
     "mxfp4_workspace_bytes", "mxfp4_status_string",
 )
 
@@ -48,6 +48,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     lib.mxfp4_quantize.argtypes = [p, i64, i64, i32, i32, i32, p, p, p]
     lib.mxfp4_quantize.restype = i32
+    lib.mxfp4_quantize_dual.argtypes = [p, i64, i64, i32, i32, p, p, p, p, p]
+    lib.mxfp4_quantize_dual.restype = i32
     lib.mxfp4_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
     lib.mxfp4_gemm.restype = i32
     for name in ("mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad"):
@@ -108,6 +110,21 @@ def mxfp4_quantize(src, rows, cols, axis, hadamard, scale_mode, out_nibbles, out
     _check(load_library().mxfp4_quantize(_ptr(src), rows, cols, axis, hadamard, scale_mode,
                                          _ptr(out_nibbles), _ptr(out_e8m0), _stream(stream)),
            "mxfp4_quantize")
+
+
+def mxfp4_quantize_dual(src, rows, cols, hadamard, scale_mode, row_nibbles, row_e8m0,
+                        col_nibbles, col_e8m0, stream=None):
+    """One read of ``src`` (bf16 [rows][cols]); row-wise and column-wise
+    transposed packed operands into caller buffers."""
+    import torch
+    _need(src, torch.bfloat16, rows * cols, "src")
+    _need(row_nibbles, torch.uint8, rows * cols // 2, "row_nibbles")
+    _need(row_e8m0, torch.uint8, rows * cols // 32, "row_e8m0")
+    _need(col_nibbles, torch.uint8, rows * cols // 2, "col_nibbles")
+    _need(col_e8m0, torch.uint8, rows * cols // 32, "col_e8m0")
+    _check(load_library().mxfp4_quantize_dual(
+        _ptr(src), rows, cols, hadamard, scale_mode, _ptr(row_nibbles), _ptr(row_e8m0),
+        _ptr(col_nibbles), _ptr(col_e8m0), _stream(stream)), "mxfp4_quantize_dual")
 
 
 def mxfp4_gemm(Aq, As, Bq, Bs, M, N, K, C, out_dtype=OUT_F32, stream=None):
@@ -188,6 +205,17 @@ def quantize(src, axis=AXIS_ROW, hadamard=16, scale_mode=SCALE_OCP_FLOOR, stream
     sc = torch.empty(ss, dtype=torch.uint8, device=src.device)
     mxfp4_quantize(src, rows, cols, axis, hadamard, scale_mode, nib, sc, stream)
     return nib, sc
+
+
+def quantize_dual(src, hadamard=16, scale_mode=SCALE_OCP_FLOOR, stream=None):
+    """Allocate outputs and quantize both orientations with one read; returns
+    ((row_nibbles, row_e8m0), (col_nibbles, col_e8m0))."""
+    import torch
+    rows, cols = src.shape
+    (rn, rs), (cn, cs) = packed_shapes(rows, cols, AXIS_ROW), packed_shapes(rows, cols, AXIS_COL)
+    out = [torch.empty(sh, dtype=torch.uint8, device=src.device) for sh in (rn, rs, cn, cs)]
+    mxfp4_quantize_dual(src, rows, cols, hadamard, scale_mode, *out, stream=stream)
+    return (out[0], out[1]), (out[2], out[3])
 
 
 def gemm(Aq, As, Bq, Bs, out_dtype=OUT_F32, stream=None):

@@ -138,6 +138,20 @@ int mxfp4_quantize(const void* src_bf16, int64_t rows, int64_t cols, int axis, i
                                         out_nibbles, out_e8m0, stream));
 }
 
+int mxfp4_quantize_dual(const void* src_bf16, int64_t rows, int64_t cols, int hadamard,
+                        int scale_mode, void* row_nibbles, void* row_e8m0, void* col_nibbles,
+                        void* col_e8m0, hipStream_t stream) {
+  int st = check_quantize(src_bf16, rows, cols, MXFP4_AXIS_ROW, hadamard, scale_mode,
+                          row_nibbles, row_e8m0);
+  if (st == MXFP4_OK)
+    st = check_quantize(src_bf16, rows, cols, MXFP4_AXIS_COL, hadamard, scale_mode, col_nibbles,
+                        col_e8m0);
+  if (st != MXFP4_OK || rows == 0 || cols == 0) return st;
+  return hip_status(mx::launch_quantize_dual(src_bf16, rows, cols, hadamard, scale_mode,
+                                             row_nibbles, row_e8m0, col_nibbles, col_e8m0,
+                                             stream));
+}
+
 int mxfp4_gemm(const void* Aq, const void* As, const void* Bq, const void* Bs, int64_t M,
                int64_t N, int64_t K, void* C, int out_dtype, hipStream_t stream) {
   const int st = check_gemm(Aq, As, Bq, Bs, M, N, K, C, out_dtype);

@@ -11,6 +11,12 @@ hipError_t launch_quantize(const void* src, int64_t rows, int64_t cols, int axis
                            int hadamard, int scale_mode, void* nib, void* sc,
                            hipStream_t stream);
 
+// One read of src, two outputs: row-wise (rnib, rsc) and column-wise
+// transposed (cnib, csc), each as launch_quantize with axis ROW / COL.
+hipError_t launch_quantize_dual(const void* src, int64_t rows, int64_t cols, int hadamard,
+                                int scale_mode, void* rnib, void* rsc, void* cnib, void* csc,
+                                hipStream_t stream);
+
 // Block-scaled MXFP4 GEMM, C[M][N] = A[M][K] B[N][K]^T.
 hipError_t launch_gemm(const void* Aq, const void* As, const void* Bq, const void* Bs,
                        int64_t M, int64_t N, int64_t K, void* C, int out_dtype,

@@ -238,27 +238,28 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
   }
 }
 
-// Staged path (rows % 128 == 0, cols % 4 == 0, 4-byte aligned scales):
-// work-group = 4 waves = 4 bands of 32 rows (a 128-row group) x 256 columns.
-// Lane l of wave w owns columns [c0, c0 + 4), c0 = group*256 + 4l, of band
-// 4*rowgroup + w and loads them with 32 8-byte loads (a wave reads 512
+// Staged path (rows % (32 NB) == 0, cols % 4 == 0, scale pointer aligned to
+// NB bytes): work-group = NB waves = NB bands of 32 rows x 256 columns, NB = 8
+// (or 4). Lane l of wave w owns columns [c0, c0 + 4), c0 = group*256 + 4l, of
+// band NB*rowgroup + w and loads them with 32 8-byte loads (a wave reads 512
 // contiguous bytes per row). The quantized bands go to LDS; the work-group
-// then writes each column's 4 bands as 64 contiguous nibble bytes and one
-// 4-byte scale word, instead of scattered 16-byte and 1-byte stores. Four
-// columns per lane keep the register count low enough for four waves per
-// SIMD, so loads of one wave overlap the arithmetic of another.
-template <int H, int MODE>
-__global__ __launch_bounds__(256) void quant_col_staged_kernel(const uint16_t* __restrict__ src,
-                                                               int64_t rows, int64_t cols,
-                                                               uint8_t* __restrict__ nib,
-                                                               uint8_t* __restrict__ sc) {
-  __shared__ __attribute__((aligned(16))) uint8_t onib[256 * 4 * 16];
-  __shared__ __attribute__((aligned(16))) uint8_t osc[256 * 4];
+// then writes each column's NB bands as 16 NB contiguous nibble bytes (with
+// NB = 8 a whole 128-byte line) and one NB-byte scale word, instead of
+// scattered 16-byte and 1-byte stores. Four columns per lane keep the
+// register count low enough for several waves per SIMD, so the loads of one
+// wave overlap the arithmetic of another.
+template <int H, int MODE, int NB>
+__global__ __launch_bounds__(64 * NB) void quant_col_staged_kernel(const uint16_t* __restrict__ src,
+                                                                   int64_t rows, int64_t cols,
+                                                                   uint8_t* __restrict__ nib,
+                                                                   uint8_t* __restrict__ sc) {
+  __shared__ __attribute__((aligned(16))) uint8_t onib[256 * NB * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t osc[256 * NB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t ncg = (cols + 255) / 256;
   const int64_t cg = (int64_t)blockIdx.x % ncg;
   const int64_t rg = (int64_t)blockIdx.x / ncg;
-  const int64_t band = rg * 4 + wave;
+  const int64_t band = rg * NB + wave;
   const int64_t c0 = cg * 256 + (int64_t)lane * 4;
   if (c0 < cols) {
     const uint16_t* p = src + band * 32 * cols + c0;
@@ -266,41 +267,43 @@ __global__ __launch_bounds__(256) void quant_col_staged_kernel(const uint16_t* _
 #pragma unroll
     for (int r = 0; r < 32; ++r) raw[r] = *reinterpret_cast<const uint2*>(p + r * cols);
 #pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
-      float a[32], b[32];
+    for (int j = 0; j < 4; ++j) {  // one column at a time keeps the register count low
+      float a[32];
 #pragma unroll
       for (int r = 0; r < 32; ++r) {
-        const uint32_t d = pr == 0 ? raw[r].x : raw[r].y;
-        a[r] = bf16lo(d);
-        b[r] = bf16hi(d);
+        const uint32_t d = j < 2 ? raw[r].x : raw[r].y;
+        a[r] = (j & 1) ? bf16hi(d) : bf16lo(d);
       }
       hadamard32<H>(a);
-      hadamard32<H>(b);
-      uint4 na, nb;
-      uint32_t sa, sb;
+      uint4 na;
+      uint32_t sa;
       encode_block<MODE>(a, na, sa);
-      encode_block<MODE>(b, nb, sb);
-      const int ca = lane * 4 + 2 * pr, cb = ca + 1;
-      *reinterpret_cast<uint4*>(onib + (ca * 4 + wave) * 16) = na;
-      *reinterpret_cast<uint4*>(onib + (cb * 4 + wave) * 16) = nb;
-      osc[ca * 4 + wave] = (uint8_t)sa;
-      osc[cb * 4 + wave] = (uint8_t)sb;
+      const int ca = lane * 4 + j;
+      *reinterpret_cast<uint4*>(onib + (ca * NB + wave) * 16) = na;
+      osc[ca * NB + wave] = (uint8_t)sa;
     }
   }
   __syncthreads();
   const int64_t npitch = rows / 2, spitch = rows / 32;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int q = threadIdx.x + 256 * i;  // 16-byte chunk: column q / 4, band q % 4
-    const int64_t col = cg * 256 + (q >> 2);
+    const int q = threadIdx.x + 64 * NB * i;  // 16-byte chunk: column q / NB, band q % NB
+    const int64_t col = cg * 256 + q / NB;
     if (col < cols)
-      *reinterpret_cast<uint4*>(nib + col * npitch + rg * 64 + (q & 3) * 16) =
+      *reinterpret_cast<uint4*>(nib + col * npitch + rg * 16 * NB + (q % NB) * 16) =
           *reinterpret_cast<const uint4*>(onib + q * 16);
   }
-  const int64_t col = cg * 256 + threadIdx.x;
-  if (col < cols)
-    *reinterpret_cast<uint32_t*>(sc + col * spitch + rg * 4) =
-        *reinterpret_cast<const uint32_t*>(osc + threadIdx.x * 4);
+  if (threadIdx.x < 256) {
+    const int64_t col = cg * 256 + threadIdx.x;
+    if (col < cols) {
+      if constexpr (NB == 8)
+        *reinterpret_cast<uint2*>(sc + col * spitch + rg * 8) =
+            *reinterpret_cast<const uint2*>(osc + threadIdx.x * 8);
+      else
+        *reinterpret_cast<uint32_t*>(sc + col * spitch + rg * 4) =
+            *reinterpret_cast<const uint32_t*>(osc + threadIdx.x * 4);
+    }
+  }
 }
 
 // Scalar path for any cols: one thread per (column, 32-row band); loads are
@@ -325,6 +328,161 @@ __global__ __launch_bounds__(256) void quant_col_scalar_kernel(const uint16_t* _
   sc[c * (rows / 32) + band] = (uint8_t)s;
 }
 
+// ------------------------------------------------ dual (row + column, one read)
+// Training needs an activation both along its feature axis (Fprop, Dgrad:
+// 1x32 blocks, rotation along cols) and along the token axis (Wgrad: 32x1
+// blocks, rotation down rows, transposed output); [P1] A.2 and D quantize
+// both from the same tensor. This kernel reads the bf16 tile once and emits
+// both packed operands, each exactly as mxfp4_quantize would.
+//
+// Tiling as the staged column path (NB = 8 or 4 bands of 32 rows; here also
+// cols % 256 == 0): lane l of wave w holds columns [c0, c0 + 4) of band
+// NB*rowgroup + w in registers. Column direction: unchanged. Row direction,
+// for each of the band's 32 rows: the lane's 4 values are columns 4l + j of
+// a 32-column block spread over 8 lanes; butterfly stages 1 and 2 pair
+// values inside the lane, stages 4, 8 (and 16 for H32) pair lanes l ^ 1,
+// l ^ 2 (and l ^ 4) through DPP quad permutations (and ds_swizzle), where
+// the lane holding the lower column forms a + b and its partner a - b, the
+// same operations in the same order as the in-register butterfly. The block
+// amax is reduced over the 8 lanes; each lane encodes its 4 values into 2
+// nibble bytes. Both outputs are staged in LDS and written with 16-byte
+// nibble stores (whole 128-byte lines per row and, with NB = 8, per column)
+// and 8- or 4-byte scale stores.
+// Lane exchange inside groups of 8 lanes: partner lane l ^ M. M = 1, 2 use a
+// DPP quad permutation (lane i of a quad reads lane sel[i]); M = 4 uses
+// ds_swizzle in bit mode (lane i reads lane ((i & 0x1f) | 0) ^ 4).
+template <int M>
+__device__ __forceinline__ uint32_t xchg(uint32_t v) {
+  if constexpr (M == 1)
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+  else if constexpr (M == 2)
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+  else
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F);               // xor 4
+}
+
+template <int M>
+__device__ __forceinline__ float xchgf(float v) {
+  return __uint_as_float(xchg<M>(__float_as_uint(v)));
+}
+
+// One cross-lane butterfly stage: the lane holding the lower column forms
+// own + partner (= a + b), its partner partner + (-own) (= a - b, the same
+// fp32 operation), with the sign flip applied to the lane's own value.
+template <int M>
+__device__ __forceinline__ void row_stage(float (&x)[4], int lane) {
+  const uint32_t flip = (lane & M) ? 0x80000000u : 0u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float y = xchgf<M>(x[j]);
+    x[j] = y + __uint_as_float(__float_as_uint(x[j]) ^ flip);
+  }
+}
+
+template <int H>
+__device__ __forceinline__ void row_butterfly4(float (&x)[4], int lane) {
+  if constexpr (H != 0) {
+    float a;
+    a = x[0]; x[0] = a + x[1]; x[1] = a - x[1];
+    a = x[2]; x[2] = a + x[3]; x[3] = a - x[3];
+    a = x[0]; x[0] = a + x[2]; x[2] = a - x[2];
+    a = x[1]; x[1] = a + x[3]; x[3] = a - x[3];
+    row_stage<1>(x, lane);
+    row_stage<2>(x, lane);
+    if constexpr (H == 32) row_stage<4>(x, lane);
+    const float c = (H == 16) ? 0.25f : __uint_as_float(0x3E3504F3u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] *= c;
+  }
+}
+
+template <int H, int MODE, int NB>
+__global__ __launch_bounds__(64 * NB) void quant_dual_kernel(const uint16_t* __restrict__ src,
+                                                             int64_t rows, int64_t cols,
+                                                             uint8_t* __restrict__ rnib,
+                                                             uint8_t* __restrict__ rsc,
+                                                             uint8_t* __restrict__ cnib,
+                                                             uint8_t* __restrict__ csc) {
+  __shared__ __attribute__((aligned(16))) uint8_t onib[256 * NB * 16];  // column output
+  __shared__ __attribute__((aligned(16))) uint8_t osc[256 * NB];
+  __shared__ __attribute__((aligned(16))) uint8_t lrn[32 * NB * 128];   // row output
+  __shared__ __attribute__((aligned(16))) uint8_t lrs[32 * NB * 8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t ncg = cols / 256;
+  const int64_t cg = (int64_t)blockIdx.x % ncg;
+  const int64_t rg = (int64_t)blockIdx.x / ncg;
+  const int64_t band = rg * NB + wave;
+  const int64_t c0 = cg * 256 + (int64_t)lane * 4;
+  const uint16_t* p = src + band * 32 * cols + c0;
+  uint2 raw[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) raw[r] = *reinterpret_cast<const uint2*>(p + r * cols);
+  // row direction
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    float x[4] = {bf16lo(raw[r].x), bf16hi(raw[r].x), bf16lo(raw[r].y), bf16hi(raw[r].y)};
+    row_butterfly4<H>(x, lane);
+    uint32_t am = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) am = max(am, __float_as_uint(x[j]) & 0x7fffffffu);
+    am = max(am, xchg<1>(am));
+    am = max(am, xchg<2>(am));
+    am = max(am, xchg<4>(am));
+    const uint32_t s = e8m0_byte<MODE>(am);
+    uint32_t w = 0;
+    if (s != 255u) {
+      const float scale = scale_of_byte(s);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[0], x[1], scale, 0);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2], x[3], scale, 1);
+    }
+    const int lr = wave * 32 + r;
+    *reinterpret_cast<uint16_t*>(lrn + lr * 128 + lane * 2) = (uint16_t)w;
+    if ((lane & 7) == 0) lrs[lr * 8 + (lane >> 3)] = (uint8_t)s;
+  }
+  // column direction
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // one column at a time keeps the register count low
+    float a[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      const uint32_t d = j < 2 ? raw[r].x : raw[r].y;
+      a[r] = (j & 1) ? bf16hi(d) : bf16lo(d);
+    }
+    hadamard32<H>(a);
+    uint4 na;
+    uint32_t sa;
+    encode_block<MODE>(a, na, sa);
+    const int ca = lane * 4 + j;
+    *reinterpret_cast<uint4*>(onib + (ca * NB + wave) * 16) = na;
+    osc[ca * NB + wave] = (uint8_t)sa;
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  const int64_t npitch = rows / 2, spitch = rows / 32;
+  const int64_t rpitch = cols / 2, rspitch = cols / 32;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = t + 64 * NB * i;
+    // column output: 16-byte chunk q = (column q / NB, band q % NB)
+    *reinterpret_cast<uint4*>(cnib + (cg * 256 + q / NB) * npitch + rg * 16 * NB + (q % NB) * 16) =
+        *reinterpret_cast<const uint4*>(onib + q * 16);
+    // row output: 16-byte chunk q = (row q / 8, chunk q % 8)
+    *reinterpret_cast<uint4*>(rnib + (rg * 32 * NB + (q >> 3)) * rpitch + cg * 128 + (q & 7) * 16) =
+        *reinterpret_cast<const uint4*>(lrn + q * 16);
+  }
+  if (t < 256) {
+    if constexpr (NB == 8)
+      *reinterpret_cast<uint2*>(csc + (cg * 256 + t) * spitch + rg * 8) =
+          *reinterpret_cast<const uint2*>(osc + t * 8);
+    else
+      *reinterpret_cast<uint32_t*>(csc + (cg * 256 + t) * spitch + rg * 4) =
+          *reinterpret_cast<const uint32_t*>(osc + t * 4);
+  }
+  if (t < 32 * NB)
+    *reinterpret_cast<uint2*>(rsc + (rg * 32 * NB + t) * rspitch + cg * 8) =
+        *reinterpret_cast<const uint2*>(lrs + t * 8);
+}
+
 template <int H, int MODE>
 hipError_t dispatch_axis(const void* src, int64_t rows, int64_t cols, int axis, void* nib,
                          void* sc, hipStream_t st) {
@@ -336,9 +494,14 @@ hipError_t dispatch_axis(const void* src, int64_t rows, int64_t cols, int axis, 
                        static_cast<const uint4*>(src), nblocks, static_cast<uint4*>(nib),
                        static_cast<uint8_t*>(sc));
   } else if (axis == 1) {
-    if (rows % 128 == 0 && cols % 4 == 0 && ((uintptr_t)sc % 4 == 0)) {
+    if (rows % 256 == 0 && cols % 4 == 0 && ((uintptr_t)sc % 8 == 0)) {
+      const int64_t grid = (rows / 256) * ((cols + 255) / 256);
+      hipLaunchKernelGGL((quant_col_staged_kernel<H, MODE, 8>), dim3((unsigned)grid), dim3(512),
+                         0, st, static_cast<const uint16_t*>(src), rows, cols,
+                         static_cast<uint8_t*>(nib), static_cast<uint8_t*>(sc));
+    } else if (rows % 128 == 0 && cols % 4 == 0 && ((uintptr_t)sc % 4 == 0)) {
       const int64_t grid = (rows / 128) * ((cols + 255) / 256);
-      hipLaunchKernelGGL((quant_col_staged_kernel<H, MODE>), dim3((unsigned)grid), blk, 0, st,
+      hipLaunchKernelGGL((quant_col_staged_kernel<H, MODE, 4>), dim3((unsigned)grid), blk, 0, st,
                          static_cast<const uint16_t*>(src), rows, cols,
                          static_cast<uint8_t*>(nib), static_cast<uint8_t*>(sc));
     } else if (cols % 8 == 0) {
@@ -368,6 +531,28 @@ hipError_t dispatch_mode(const void* src, int64_t rows, int64_t cols, int axis, 
                        : dispatch_axis<H, kOcpFloor>(src, rows, cols, axis, nib, sc, st);
 }
 
+template <int H, int MODE>
+hipError_t dispatch_dual(const void* src, int64_t rows, int64_t cols, void* rnib, void* rsc,
+                         void* cnib, void* csc, hipStream_t st) {
+  const bool fast = rows % 128 == 0 && cols % 256 == 0 && ((uintptr_t)rsc % 8 == 0) &&
+                    ((uintptr_t)csc % 4 == 0);
+  if (!fast) {
+    hipError_t e = dispatch_axis<H, MODE>(src, rows, cols, 0, rnib, rsc, st);
+    if (e != hipSuccess) return e;
+    return dispatch_axis<H, MODE>(src, rows, cols, 1, cnib, csc, st);
+  }
+  const auto* s16 = static_cast<const uint16_t*>(src);
+  auto* rn = static_cast<uint8_t*>(rnib);
+  auto* rs = static_cast<uint8_t*>(rsc);
+  auto* cn = static_cast<uint8_t*>(cnib);
+  auto* cs = static_cast<uint8_t*>(csc);
+  // Four bands per work-group: with both outputs staged, eight bands would
+  // take 68 KB of LDS per work-group and leave too few waves per CU.
+  hipLaunchKernelGGL((quant_dual_kernel<H, MODE, 4>), dim3((unsigned)((rows / 128) * (cols / 256))),
+                     dim3(256), 0, st, s16, rows, cols, rn, rs, cn, cs);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const void* src, int64_t rows, int64_t cols, int axis, int hadamard,
@@ -376,6 +561,20 @@ hipError_t launch_quantize(const void* src, int64_t rows, int64_t cols, int axis
     case 16: return dispatch_mode<16>(src, rows, cols, axis, scale_mode, nib, sc, stream);
     case 32: return dispatch_mode<32>(src, rows, cols, axis, scale_mode, nib, sc, stream);
     default: return dispatch_mode<0>(src, rows, cols, axis, scale_mode, nib, sc, stream);
+  }
+}
+
+hipError_t launch_quantize_dual(const void* src, int64_t rows, int64_t cols, int hadamard,
+                                int scale_mode, void* rnib, void* rsc, void* cnib, void* csc,
+                                hipStream_t stream) {
+  const bool ceil = scale_mode == kCeil;
+  switch (hadamard) {
+    case 16: return ceil ? dispatch_dual<16, kCeil>(src, rows, cols, rnib, rsc, cnib, csc, stream)
+                         : dispatch_dual<16, kOcpFloor>(src, rows, cols, rnib, rsc, cnib, csc, stream);
+    case 32: return ceil ? dispatch_dual<32, kCeil>(src, rows, cols, rnib, rsc, cnib, csc, stream)
+                         : dispatch_dual<32, kOcpFloor>(src, rows, cols, rnib, rsc, cnib, csc, stream);
+    default: return ceil ? dispatch_dual<0, kCeil>(src, rows, cols, rnib, rsc, cnib, csc, stream)
+                         : dispatch_dual<0, kOcpFloor>(src, rows, cols, rnib, rsc, cnib, csc, stream);
   }
 }
 

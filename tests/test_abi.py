@@ -109,6 +109,25 @@ def test_quantize_validation(lib):
     assert q(lib, axis=1, cols=0, src=NULL, nib=NULL, sc=NULL) == 0
 
 
+def qd(lib, src=FAKE, rows=64, cols=64, h=16, mode=0, rn=FAKE, rs=FAKE, cn=FAKE, cs=FAKE):
+    return lib.mxfp4_quantize_dual(src, rows, cols, h, mode, rn, rs, cn, cs, NULL)
+
+
+def test_quantize_dual_validation(lib):
+    assert qd(lib, h=8) == 3
+    assert qd(lib, mode=5) == 3
+    assert qd(lib, cols=48) == 2               # row orientation: cols % 32
+    assert qd(lib, rows=48) == 2               # column orientation: rows % 32
+    assert qd(lib, rows=-32) == 2
+    for kw in ("src", "rn", "rs", "cn", "cs"):
+        assert qd(lib, **{kw: NULL}) == 1, kw
+    assert qd(lib, src=FAKE_ODD) == 6
+    assert qd(lib, rn=FAKE_ODD) == 6
+    assert qd(lib, cn=FAKE_ODD) == 6
+    assert qd(lib, rows=0, src=NULL, rn=NULL, rs=NULL, cn=NULL, cs=NULL) == 0
+    assert qd(lib, cols=0, src=NULL, rn=NULL, rs=NULL, cn=NULL, cs=NULL) == 0
+
+
 def g(lib, M=64, N=64, K=64, out=0, A=FAKE, As=FAKE, B=FAKE, Bs=FAKE, C=FAKE):
     return lib.mxfp4_gemm(A, As, B, Bs, M, N, K, C, out, NULL)
 

@@ -133,3 +133,50 @@ def test_quantizer_workload_full_size(quant_workload, axis, mode):
 @pytest.mark.parametrize("h", [0, 32])
 def test_quantizer_workload_full_size_other_rotations(quant_workload, h):
     assert_same(quant_workload, 0, h, 0, f"full row h={h}")
+
+
+# ------------------------------------------------------- dual orientation
+def run_gpu_dual(bits, h, mode):
+    import torch
+    import mxfp4_quantized_gemm_amd as mx
+    x = to_dev_bf16(bits)
+    (rn, rs), (cn, cs) = mx.quantize_dual(x, h, mode)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in (rn, rs, cn, cs)]
+
+
+def assert_dual_same(bits, h, mode, what=""):
+    rn, rs, cn, cs = run_gpu_dual(bits, h, mode)
+    orn, ors = O.quantize_chunked(bits, 0, h, mode)
+    ocn, ocs = O.quantize_chunked(bits, 1, h, mode)
+    for got, want, name in ((rn, orn, "row nibbles"), (rs, ors, "row scales"),
+                            (cn, ocn, "col nibbles"), (cs, ocs, "col scales")):
+        assert got.shape == want.shape, f"{what} {name}"
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, f"{what}: {len(bad)} {name} bytes differ, first {bad[:4].tolist()}"
+
+
+# one-read kernel (rows % 128, cols % 256) and the two-kernel path otherwise
+DUAL_SHAPES = [(128, 256), (256, 512), (384, 1280), (128, 4096), (32, 32), (96, 160), (128, 288)]
+
+
+@pytest.mark.parametrize("h", [0, 16, 32])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_dual_small_shapes_bit_exact(h, mode):
+    for i, (r, c) in enumerate(DUAL_SHAPES):
+        bits = heavy(r, c, 4000 + 11 * i)
+        assert_dual_same(bits, h, mode, f"dual h={h} mode={mode} shape={(r, c)}")
+
+
+@pytest.mark.parametrize("h", [0, 16, 32])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_dual_edge_values_bit_exact(h, mode):
+    # special blocks along rows (first half) and, transposed, down columns (second half)
+    bits = np.concatenate([edge_matrix(128, 256, seed=9), edge_matrix(256, 128, seed=10).T], 0)
+    bits = np.ascontiguousarray(bits)
+    assert_dual_same(bits, h, mode, f"dual edge h={h} mode={mode}")
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_dual_quantizer_workload_full_size(quant_workload, mode):
+    assert_dual_same(quant_workload, 16, mode, f"dual full mode={mode}")
