@@ -365,6 +365,49 @@ def error_decomposition(x_blocks: np.ndarray, mode: int) -> dict:
             "e_grid": e_grid, "deadzone": dz, "E": E, "m_b": m_b}
 
 
+STAT_FIELDS = ("sum_e_scale2", "sum_e_dz2", "sum_e_grid2", "dot_scale_grid", "dot_scale_dz",
+               "sum_e2", "sum_x2", "n_deadzone", "n_elements", "n_nonfinite_blocks")
+
+
+def error_stats(src_bf16: np.ndarray, axis: int, hadamard: int, mode: int) -> dict:
+    """Tensor-level sums of the three-way decomposition of the MXFP4 error of
+    the values ``quantize`` encodes (the rotated operand), over its 1x32
+    (row) or 32x1 (col) blocks ([P3] core insight and Property 1; the
+    deadzone share is the statistic [P3] reports for weights):
+    sum e_scale^2, sum e_DZ^2, sum e_grid^2, sum e_scale e_grid,
+    sum e_scale e_DZ, sum e^2, sum x^2, deadzone count, element count.
+    Blocks holding a non-finite rotated value are left out and counted.
+    """
+    x = bf16_to_f32(src_bf16)
+    if axis == AXIS_COL:
+        x = np.ascontiguousarray(x.T)
+    elif axis != AXIS_ROW:
+        raise ValueError("error statistics are defined for 1x32 and 32x1 blocks")
+    y = hadamard_rotate(x, hadamard).reshape(-1, BLOCK)
+    finite = np.all(np.isfinite(y), axis=1)
+    d = error_decomposition(y[finite], mode)
+    es, edz, eg, e = d["e_scale"], d["e_dz"], d["e_grid"], d["e"]
+    x64 = y[finite].astype(np.float64)
+    vals = (np.sum(es * es), np.sum(edz * edz), np.sum(eg * eg), np.sum(es * eg),
+            np.sum(es * edz), np.sum(e * e), np.sum(x64 * x64), np.count_nonzero(d["deadzone"]),
+            x64.size, np.count_nonzero(~finite))
+    return {k: float(v) for k, v in zip(STAT_FIELDS, vals)}
+
+
+def error_stats_chunked(src_bf16: np.ndarray, axis: int, hadamard: int, mode: int,
+                        chunk: int = 512) -> dict:
+    """``error_stats`` summed over slabs (rows for row blocks, columns for
+    column blocks) to bound memory; blocks never straddle slabs."""
+    r, c = src_bf16.shape
+    if axis == AXIS_COL:
+        parts = [error_stats(src_bf16[:, j:j + chunk], axis, hadamard, mode)
+                 for j in range(0, c, chunk)]
+    else:
+        parts = [error_stats(src_bf16[i:i + chunk], axis, hadamard, mode)
+                 for i in range(0, r, chunk)]
+    return {k: float(sum(p[k] for p in parts)) for k in STAT_FIELDS}
+
+
 def error_report(C: np.ndarray, P: np.ndarray) -> dict:
     """MSE, cosine, relative Frobenius error and SNR (dB) of C against P."""
     C = np.asarray(C, dtype=np.float64)

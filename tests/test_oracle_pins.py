@@ -456,6 +456,64 @@ def test_floor_mode_breaks_the_lemma_premise():
     assert dc["E"][0] == 1 and dc["Q"][0, 1] == 0.0
 
 
+# ----------------------------------------------- tensor-level error sums
+def _stat_src(rows=256, cols=512, seed=21):
+    rng = np.random.default_rng(seed)
+    a = rng.standard_t(3, size=(rows, cols)) * rng.lognormal(0, 1, size=(1, cols))
+    return synthetic.f64_to_bf16_bits(a)
+
+
+@pytest.mark.parametrize("axis", [O.AXIS_ROW, O.AXIS_COL])
+@pytest.mark.parametrize("mode", [O.MODE_OCP_FLOOR, O.MODE_CEIL])
+@pytest.mark.parametrize("h", [0, 16, 32])
+def test_error_stats_pins(axis, mode, h):
+    """error_stats against what fixes it independently: (1) sum e^2 is the
+    squared error of the packed operand itself (dequantize(quantize(src))
+    against the rotated source, a different code path); (2) the MSE
+    identity of [P3] Property 1 with both cross terms; (3) in ceil mode
+    <e_DZ, e_scale> = 0 exactly; (4) the deadzone count is bounded by the
+    zero codes in ceil mode (deadzone values quantize to 0) and counts
+    elements with 24|x| < m_b; (5) the element count."""
+    src = _stat_src()
+    st = O.error_stats(src, axis, h, mode)
+    x = O.bf16_to_f32(src)
+    if axis == O.AXIS_COL:
+        x = np.ascontiguousarray(x.T)
+    y = O.hadamard_rotate(x, h).astype(np.float64)
+    nib, sc = O.quantize(src, axis, h, mode)
+    deq = O.dequantize(nib, sc)
+    e2 = float(np.sum((deq - y) ** 2))
+    assert st["sum_e2"] == pytest.approx(e2, rel=1e-12)
+    rhs = (st["sum_e_scale2"] + st["sum_e_dz2"] + st["sum_e_grid2"] + 2 * st["dot_scale_grid"]
+           + 2 * st["dot_scale_dz"])
+    assert st["sum_e2"] == pytest.approx(rhs, rel=1e-10)
+    if mode == O.MODE_CEIL:
+        assert st["dot_scale_dz"] == 0.0
+        assert st["n_deadzone"] <= np.count_nonzero(deq == 0.0)
+    blocks = y.reshape(-1, 32)
+    mb = np.max(np.abs(blocks), axis=1, keepdims=True)
+    assert st["n_deadzone"] == np.count_nonzero(24.0 * np.abs(blocks) < mb)
+    assert st["n_elements"] == src.size and st["n_nonfinite_blocks"] == 0
+    assert st["sum_x2"] == pytest.approx(float(np.sum(y * y)), rel=1e-12)
+
+
+def test_error_stats_skips_nonfinite_blocks_and_chunks_agree():
+    src = _stat_src(128, 256, 5)
+    src[3, 40] = 0x7FC0   # NaN in row 3, block 1
+    src[70, 5] = 0x7F80   # +Inf in row 70, block 0
+    st = O.error_stats(src, O.AXIS_ROW, 16, O.MODE_CEIL)
+    assert st["n_nonfinite_blocks"] == 2 and st["n_elements"] == src.size - 64
+    assert np.isfinite(st["sum_e2"])
+    ch = O.error_stats_chunked(src, O.AXIS_ROW, 16, O.MODE_CEIL, chunk=32)
+    for k in O.STAT_FIELDS:
+        assert ch[k] == pytest.approx(st[k], rel=1e-12, abs=0)
+    stc = O.error_stats(src, O.AXIS_COL, 16, O.MODE_CEIL)
+    chc = O.error_stats_chunked(src, O.AXIS_COL, 16, O.MODE_CEIL, chunk=64)
+    assert stc["n_nonfinite_blocks"] == 2
+    for k in O.STAT_FIELDS:
+        assert chc[k] == pytest.approx(stc[k], rel=1e-12, abs=0)
+
+
 # ------------------------------------------------------- hand-worked blocks
 def test_hand_worked_blocks():
     """Blocks whose encodings follow from the definitions by hand."""
