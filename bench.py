@@ -164,6 +164,50 @@ def error_report(mx, torch, prods, stream, dev, rows=128):
     return out
 
 
+def error_decomposition(mx, torch, synthetic, np, prods, stream, dev):
+    """GPU three-way error decomposition (mxfp4_error_stats) of the quantizer
+    workload (row and column blocks, H0/H16/H32 x both scale rules) and of
+    every product operand as its fused entry quantizes it (H16, both rules):
+    cos(e_scale, e_grid), deadzone fraction and the shares of ||e||^2.
+    Also times the statistics kernel on the 8192 x 4096 tensor."""
+    def summary(d):
+        e2 = d["sum_e2"]
+        return {"cos_scale_grid": round(d["cos_scale_grid"], 4),
+                "deadzone_fraction": round(d["deadzone_fraction"], 4),
+                "scale_share": round(d["sum_e_scale2"] / e2, 4) if e2 else None,
+                "dz_share": round(d["sum_e_dz2"] / e2, 4) if e2 else None,
+                "grid_share": round(d["sum_e_grid2"] / e2, 4) if e2 else None,
+                "rel_err": round((e2 / d["sum_x2"]) ** 0.5, 5) if d["sum_x2"] else None}
+    ws = torch.empty(mx.ERROR_STATS_WS_BYTES, dtype=torch.uint8, device=dev)
+    A = synthetic.make("quant")["A"]
+    a = torch.from_numpy(A.view(np.int16)).to(dev).view(torch.bfloat16)
+    out = {"quant_8192x4096": {}}
+    for ax in (0, 1):
+        for h in (0, 16, 32):
+            for m in (0, 1):
+                d = mx.error_stats(a, ax, h, m, stream, ws)
+                out["quant_8192x4096"][f"{['row', 'col'][ax]}_h{h}_{['ocp_floor', 'ceil'][m]}"] = summary(d)
+    for p in prods:
+        for which, t, shape, ax in (("A", p["P"], p["sa"], p["axa"]), ("B", p["Q"], p["sb"], p["axb"])):
+            for m in (0, 1):
+                d = mx.error_stats(t.view(shape[0], shape[1]), ax, 16, m, stream, ws)
+                out.setdefault(p["name"], {})[f"{which}_h16_{['ocp_floor', 'ceil'][m]}"] = summary(d)
+    o = torch.empty(mx.ERROR_STATS_COUNT, dtype=torch.float64, device=dev)
+    R, C = A.shape
+    for _ in range(3):
+        mx.mxfp4_error_stats(a, R, C, 0, 16, 0, ws, o, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(20):
+        mx.mxfp4_error_stats(a, R, C, 0, 16, 0, ws, o, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / 20 * 1e3
+    out["kernel_row_h16_us"] = round(us, 2)
+    out["kernel_row_h16_GB/s"] = round(2.0 * R * C / (us * 1e-6) / 1e9, 1)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -424,9 +468,10 @@ def main():
         log("quantizer arms done")
 
     # ------------------------------------------------------- error report
-    errs = None
+    errs = decomp = None
     if not args.no_error_report:
         errs = error_report(mx, torch, prods, stream, dev)
+        decomp = error_decomposition(mx, torch, synthetic, np, prods, stream, dev)
         log("error report done")
 
     # -------------------------------------------------------------- roofline
@@ -460,6 +505,7 @@ def main():
         "kernels": kernels,
         "quantizer": quant,
         "error_report": errs,
+        "error_decomposition": decomp,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -126,6 +126,37 @@ int mxfp4_quantize_dual(const void* src_bf16, int64_t rows, int64_t cols,
                         void* col_nibbles, void* col_e8m0, hipStream_t stream);
 
 /*
+ * mxfp4_error_stats -- tensor-level decomposition of the MXFP4 error of the
+ * operand mxfp4_quantize would produce ([P3] core insight: ideal scale
+ * s* = m_b / 6, e = e_scale + e_DZ + e_grid, deadzone |x| < m_b / 24;
+ * [P3] Property 1: orthogonality and the MSE identity).
+ *
+ * For every 1x32 (axis MXFP4_AXIS_ROW) or 32x1 (MXFP4_AXIS_COL) block of
+ * the rotated source x (fp32, as mxfp4_quantize computes it) with amax m_b:
+ * Q = the block's dequantized MXFP4 values (E8M0 by scale_mode, E2M1 codes);
+ * Q* = s* * nearest E2M1 value of x / s* (ties to the even code, clamp 6),
+ * computed in fp64; D = {i : 24 |x_i| < m_b}; e_scale = Q - Q*,
+ * e_DZ = (Q* - x) on D, e_grid = (Q* - x) off D, e = Q - x.
+ * out_stats (DEVICE, 10 doubles, 8-byte aligned) receives, summed over the
+ * tensor in fp64:
+ *   [0] sum e_scale^2   [1] sum e_DZ^2    [2] sum e_grid^2
+ *   [3] sum e_scale*e_grid               [4] sum e_scale*e_DZ
+ *   [5] sum e^2         [6] sum x^2       [7] deadzone count
+ *   [8] elements counted                 [9] blocks skipped (non-finite)
+ * Blocks holding a non-finite rotated value are skipped. The sums are added
+ * in a fixed order: repeated calls give identical bits. ws: caller
+ * workspace of at least MXFP4_ERROR_STATS_WS_BYTES (16-byte aligned).
+ * axis MXFP4_AXIS_2D32 returns MXFP4_ERR_MODE; shapes, hadamard, scale_mode
+ * and the src alignment as mxfp4_quantize. rows == 0 or cols == 0 writes
+ * zeros. Two launches on `stream`.
+ */
+#define MXFP4_ERROR_STATS_COUNT 10
+#define MXFP4_ERROR_STATS_WS_BYTES (1024 * MXFP4_ERROR_STATS_COUNT * 8)
+int mxfp4_error_stats(const void* src_bf16, int64_t rows, int64_t cols, int axis,
+                      int hadamard, int scale_mode, void* ws, size_t ws_bytes,
+                      double* out_stats, hipStream_t stream);
+
+/*
  * mxfp4_gemm -- C[M][N] = sum_k deqA[m][k] * deqB[n][k] on gfx950's
  * block-scaled FP4 MFMA with FP32 accumulation ([P1] A.2; [P3]).
  *

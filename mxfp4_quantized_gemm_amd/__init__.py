@@ -19,11 +19,16 @@ AXIS_ROW, AXIS_COL, AXIS_2D32 = 0, 1, 2
 SCALE_OCP_FLOOR, SCALE_CEIL = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 OP_FPROP, OP_DGRAD, OP_WGRAD = 0, 1, 2
+ERROR_STATS_COUNT = 10
+ERROR_STATS_WS_BYTES = 1024 * ERROR_STATS_COUNT * 8
+ERROR_STATS_FIELDS = ("sum_e_scale2", "sum_e_dz2", "sum_e_grid2", "dot_scale_grid",
+                      "dot_scale_dz", "sum_e2", "sum_x2", "n_deadzone", "n_elements",
+                      "n_nonfinite_blocks")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp4.so")
 
 EXPORTS = (
-    "mxfp4_quantize", "mxfp4_quantize_dual", "mxfp4_gemm", "mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad",
+    "mxfp4_quantize", "mxfp4_quantize_dual", "mxfp4_error_stats", "mxfp4_gemm", "mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad",
     "mxfp4_workspace_bytes", "mxfp4_status_string",
 )
 
@@ -50,6 +55,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mxfp4_quantize.restype = i32
     lib.mxfp4_quantize_dual.argtypes = [p, i64, i64, i32, i32, p, p, p, p, p]
     lib.mxfp4_quantize_dual.restype = i32
+    lib.mxfp4_error_stats.argtypes = [p, i64, i64, i32, i32, i32, p, sz, p, p]
+    lib.mxfp4_error_stats.restype = i32
     lib.mxfp4_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
     lib.mxfp4_gemm.restype = i32
     for name in ("mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad"):
@@ -125,6 +132,18 @@ def mxfp4_quantize_dual(src, rows, cols, hadamard, scale_mode, row_nibbles, row_
     _check(load_library().mxfp4_quantize_dual(
         _ptr(src), rows, cols, hadamard, scale_mode, _ptr(row_nibbles), _ptr(row_e8m0),
         _ptr(col_nibbles), _ptr(col_e8m0), _stream(stream)), "mxfp4_quantize_dual")
+
+
+def mxfp4_error_stats(src, rows, cols, axis, hadamard, scale_mode, ws, out_stats, stream=None):
+    """Error-decomposition sums of the quantized ``src`` into ``out_stats``
+    (float64, 10 values; see the header for their order)."""
+    import torch
+    _need(src, torch.bfloat16, rows * cols, "src")
+    _need(ws, torch.uint8, ERROR_STATS_WS_BYTES, "ws")
+    _need(out_stats, torch.float64, ERROR_STATS_COUNT, "out_stats")
+    _check(load_library().mxfp4_error_stats(_ptr(src), rows, cols, axis, hadamard, scale_mode,
+                                            _ptr(ws), ws.numel(), _ptr(out_stats),
+                                            _stream(stream)), "mxfp4_error_stats")
 
 
 def mxfp4_gemm(Aq, As, Bq, Bs, M, N, K, C, out_dtype=OUT_F32, stream=None):
@@ -216,6 +235,24 @@ def quantize_dual(src, hadamard=16, scale_mode=SCALE_OCP_FLOOR, stream=None):
     out = [torch.empty(sh, dtype=torch.uint8, device=src.device) for sh in (rn, rs, cn, cs)]
     mxfp4_quantize_dual(src, rows, cols, hadamard, scale_mode, *out, stream=stream)
     return (out[0], out[1]), (out[2], out[3])
+
+
+def error_stats(src, axis=AXIS_ROW, hadamard=16, scale_mode=SCALE_OCP_FLOOR, stream=None,
+                ws=None):
+    """Run mxfp4_error_stats; returns a dict of the ten sums plus the derived
+    cosine(e_scale, e_grid) and deadzone fraction (synchronizes)."""
+    import torch
+    rows, cols = src.shape
+    if ws is None:
+        ws = torch.empty(ERROR_STATS_WS_BYTES, dtype=torch.uint8, device=src.device)
+    out = torch.empty(ERROR_STATS_COUNT, dtype=torch.float64, device=src.device)
+    mxfp4_error_stats(src, rows, cols, axis, hadamard, scale_mode, ws, out, stream)
+    v = out.cpu().tolist()
+    d = dict(zip(ERROR_STATS_FIELDS, v))
+    den = (d["sum_e_scale2"] * d["sum_e_grid2"]) ** 0.5
+    d["cos_scale_grid"] = d["dot_scale_grid"] / den if den > 0 else float("nan")
+    d["deadzone_fraction"] = d["n_deadzone"] / d["n_elements"] if d["n_elements"] else float("nan")
+    return d
 
 
 def gemm(Aq, As, Bq, Bs, out_dtype=OUT_F32, stream=None):

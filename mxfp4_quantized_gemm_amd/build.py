@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxfp4.so")
-SOURCES = ["api.cpp", "quant.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "quant.hip", "gemm.hip", "stats.hip"]
 ARCH = "gfx950"
 
 

@@ -13,6 +13,10 @@
 #include "../../include/mxfp4.h"
 #include "internal.h"
 
+static_assert(MXFP4_ERROR_STATS_WS_BYTES ==
+                  mx::kStatsMaxGroups * MXFP4_ERROR_STATS_COUNT * sizeof(double),
+              "error-statistics workspace size");
+
 namespace {
 
 constexpr int64_t kMaxDim = int64_t(1) << 31;   // per-dimension limit (grid and index math)
@@ -150,6 +154,20 @@ int mxfp4_quantize_dual(const void* src_bf16, int64_t rows, int64_t cols, int ha
   return hip_status(mx::launch_quantize_dual(src_bf16, rows, cols, hadamard, scale_mode,
                                              row_nibbles, row_e8m0, col_nibbles, col_e8m0,
                                              stream));
+}
+
+int mxfp4_error_stats(const void* src_bf16, int64_t rows, int64_t cols, int axis, int hadamard,
+                      int scale_mode, void* ws, size_t ws_bytes, double* out_stats,
+                      hipStream_t stream) {
+  if (axis != MXFP4_AXIS_ROW && axis != MXFP4_AXIS_COL) return MXFP4_ERR_MODE;
+  const int st = check_quantize(src_bf16, rows, cols, axis, hadamard, scale_mode, ws, out_stats);
+  if (st != MXFP4_OK) return st;
+  if (!ws || !out_stats || ((rows == 0 || cols == 0) ? false : !src_bf16)) return MXFP4_ERR_NULL;
+  if (ws_bytes < MXFP4_ERROR_STATS_WS_BYTES) return MXFP4_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(out_stats) & 7u) || (reinterpret_cast<uintptr_t>(ws) & 7u))
+    return MXFP4_ERR_ALIGN;
+  return hip_status(mx::launch_error_stats(src_bf16, rows, cols, axis, hadamard, scale_mode, ws,
+                                           out_stats, stream));
 }
 
 int mxfp4_gemm(const void* Aq, const void* As, const void* Bq, const void* Bs, int64_t M,

@@ -17,6 +17,13 @@ hipError_t launch_quantize_dual(const void* src, int64_t rows, int64_t cols, int
                                 int scale_mode, void* rnib, void* rsc, void* cnib, void* csc,
                                 hipStream_t stream);
 
+// Tensor-level error decomposition sums (mxfp4_error_stats): ws holds
+// kStatsMaxGroups x 10 doubles of partial sums, out receives 10 doubles.
+constexpr int kStatsMaxGroups = 1024;
+hipError_t launch_error_stats(const void* src, int64_t rows, int64_t cols, int axis,
+                              int hadamard, int scale_mode, void* ws, void* out,
+                              hipStream_t stream);
+
 // Block-scaled MXFP4 GEMM, C[M][N] = A[M][K] B[N][K]^T.
 hipError_t launch_gemm(const void* Aq, const void* As, const void* Bq, const void* Bs,
                        int64_t M, int64_t N, int64_t K, void* C, int out_dtype,

@@ -128,6 +128,27 @@ def test_quantize_dual_validation(lib):
     assert qd(lib, cols=0, src=NULL, rn=NULL, rs=NULL, cn=NULL, cs=NULL) == 0
 
 
+def es(lib, src=FAKE, rows=64, cols=64, axis=0, h=16, mode=0, ws=FAKE, wsb=None, out=FAKE):
+    wsb = mx.ERROR_STATS_WS_BYTES if wsb is None else wsb
+    return lib.mxfp4_error_stats(src, rows, cols, axis, h, mode, ws, wsb, out, NULL)
+
+
+def test_error_stats_validation(lib):
+    assert "MXFP4_ERROR_STATS_WS_BYTES (1024 * MXFP4_ERROR_STATS_COUNT * 8)" in header_text()
+    assert "MXFP4_ERROR_STATS_COUNT 10" in header_text() and mx.ERROR_STATS_COUNT == 10
+    assert es(lib, axis=2) == 3                # 2D blocks have no per-block decomposition here
+    assert es(lib, h=8) == 3
+    assert es(lib, mode=2) == 3
+    assert es(lib, cols=48) == 2
+    assert es(lib, axis=1, rows=48) == 2
+    assert es(lib, src=NULL) == 1
+    assert es(lib, ws=NULL) == 1
+    assert es(lib, out=NULL) == 1
+    assert es(lib, wsb=mx.ERROR_STATS_WS_BYTES - 1) == 4
+    assert es(lib, src=FAKE_ODD) == 6
+    assert es(lib, out=ctypes.c_void_p(0x10004)) == 6
+
+
 def g(lib, M=64, N=64, K=64, out=0, A=FAKE, As=FAKE, B=FAKE, Bs=FAKE, C=FAKE):
     return lib.mxfp4_gemm(A, As, B, Bs, M, N, K, C, out, NULL)
 
