@@ -225,6 +225,43 @@ def quantize_chunked(src_bf16: np.ndarray, axis: int, hadamard: int, mode: int,
 
 
 # --------------------------------------------------------------------------
+# Outlier fallback ([P3] "three targeted fixes" section, OF: two-step
+# residual quantization x_OF = Q(x) + alpha Q(x - Q(x)), alpha = 0.5)
+# --------------------------------------------------------------------------
+OF_ALPHA = 0.5
+
+
+def quantize_of(src_bf16: np.ndarray, axis: int, hadamard: int, mode: int):
+    """OF operand of a bf16 matrix as one K-concatenated packed operand.
+
+    y = the rotated values ``quantize`` encodes (row or col axis);
+    q1 = Q(y) (this module's quantizer, ``mode``); r = fl32(y - q1);
+    q2 = Q(fl32(alpha r)) with alpha = 1/2 applied as a prescale of the
+    residual (equal to alpha Q(r) whenever the residual block's scale is
+    above the E8M0 floor, the only place the two can differ).
+    Returns (nibbles [R][2 Kb/2], scales [R][2 Kb/32]): row i holds q1's
+    row followed by q2's row, so a GEMM of depth 2 Kb against the other
+    operand repeated twice along K computes sum (q1 + q2) b. A block with a
+    non-finite rotated value is 0xFF in both halves.
+    """
+    x = bf16_to_f32(src_bf16)
+    if axis == AXIS_COL:
+        x = np.ascontiguousarray(x.T)
+    elif axis != AXIS_ROW:
+        raise ValueError("OF is defined here for 1x32 and 32x1 blocks")
+    if x.shape[1] % BLOCK:
+        raise ValueError("blocked axis must be a multiple of 32")
+    y = hadamard_rotate(x, hadamard)
+    n1, s1 = _quantize_rows(y, mode)
+    q1 = dequantize(n1, s1)                       # exact in fp32 where finite
+    with np.errstate(invalid="ignore"):
+        r = (y - q1.astype(np.float32)).astype(np.float32)
+        h = (np.float32(OF_ALPHA) * r).astype(np.float32)
+    n2, s2 = _quantize_rows(h, mode)
+    return np.concatenate([n1, n2], axis=1), np.concatenate([s1, s2], axis=1)
+
+
+# --------------------------------------------------------------------------
 # Reconstruction ([P1] quick-read block: x_rec = 2^E * Q_FP4(x / 2^E))
 # --------------------------------------------------------------------------
 def dequantize(nib: np.ndarray, sc: np.ndarray, two_d: bool = False) -> np.ndarray:

@@ -514,6 +514,55 @@ def test_error_stats_skips_nonfinite_blocks_and_chunks_agree():
         assert chc[k] == pytest.approx(stc[k], rel=1e-12, abs=0)
 
 
+# ------------------------------------------------------- outlier fallback
+@pytest.mark.parametrize("axis", [O.AXIS_ROW, O.AXIS_COL])
+@pytest.mark.parametrize("mode", [O.MODE_OCP_FLOOR, O.MODE_CEIL])
+def test_of_first_half_is_the_plain_operand(axis, mode):
+    src = _stat_src(128, 256, 31)
+    n, s = O.quantize_of(src, axis, 16, mode)
+    n1, s1 = O.quantize(src, axis, 16, mode)
+    kb = n1.shape[1]
+    assert n.shape == (n1.shape[0], 2 * kb) and s.shape == (s1.shape[0], 2 * s1.shape[1])
+    assert np.array_equal(n[:, :kb], n1) and np.array_equal(s[:, :s1.shape[1]], s1)
+
+
+def test_of_hand_worked_deadzone_rescue():
+    """[P3] OF: the outlier sets the first scale and 0.1 falls in the deadzone
+    (code 0); the residual {0, 0.1} quantized at half weight brings it back.
+    Block {6, 0.10009765625 (bf16 of 0.1), 0, ...}, no rotation:
+    ceil:  q1 = {6, 0} (E = 0); r/2 = 0.050048828125, E = -6 (6 * 2^-6 =
+           0.09375 >= r/2 > 6 * 2^-7), r/2 / 2^-6 = 3.203 -> 3 -> 0.046875.
+    floor: E = -7 (r/2 = 1.6 * 2^-5), 6.406 saturates to 6 -> 0.046875."""
+    blk = np.zeros((1, 32), dtype=np.uint16)
+    blk[0, 0] = synthetic.f64_to_bf16_bits(np.array([6.0]))[0]
+    blk[0, 1] = synthetic.f64_to_bf16_bits(np.array([0.1]))[0]
+    assert O.bf16_to_f32(blk)[0, 1] == np.float32(0.10009765625)
+    for mode, e2 in ((O.MODE_CEIL, -6), (O.MODE_OCP_FLOOR, -7)):
+        n, s = O.quantize_of(blk, O.AXIS_ROW, 0, mode)
+        d = O.dequantize(n, s)
+        assert s[0, 0] == 127 and s[0, 1] == 127 + e2
+        assert d[0, 0] == 6.0 and d[0, 1] == 0.0
+        assert d[0, 32] == 0.0 and d[0, 33] == 0.046875
+        assert np.all(d[0, 34:] == 0) and np.all(d[0, 2:32] == 0)
+
+
+def test_of_reduces_the_error_and_keeps_nonfinite_blocks():
+    src = _stat_src(256, 512, 3)
+    for mode in (O.MODE_OCP_FLOOR, O.MODE_CEIL):
+        n, s = O.quantize_of(src, O.AXIS_ROW, 16, mode)
+        y = O.hadamard_rotate(O.bf16_to_f32(src), 16).astype(np.float64)
+        d = O.dequantize(n, s)
+        of = d[:, :512] + d[:, 512:]
+        plain = O.dequantize(*O.quantize(src, O.AXIS_ROW, 16, mode))
+        # half-weight residual: the error roughly quarters
+        assert np.mean((of - y) ** 2) < 0.35 * np.mean((plain - y) ** 2)
+    bad = src.copy()
+    bad[5, 70] = 0x7FC0
+    n, s = O.quantize_of(bad, O.AXIS_ROW, 16, O.MODE_CEIL)
+    assert s[5, 2] == 255 and s[5, 16 + 2] == 255
+    assert np.all(n[5, 32:48] == 0) and np.all(n[5, 256 + 32:256 + 48] == 0)
+
+
 # ------------------------------------------------------- hand-worked blocks
 def test_hand_worked_blocks():
     """Blocks whose encodings follow from the definitions by hand."""
