@@ -158,6 +158,24 @@ def error_report(mx, torch, prods, stream, dev, rows=128):
                     "cosine": float((c * ref).sum() / (c.norm() * ref.norm())),
                     "rel_fro": (nd / nr) ** 0.5,
                     "snr_db": 10.0 * np.log10(nr / nd)}
+        if p["op"] == "fprop":
+            # outlier fallback on the weight: Y = [X | X] . [W1 | W2]^T over 2K
+            for m in (0, 1):
+                an, asc = mx.quantize(p["P"], mx.AXIS_ROW, 16, m, stream)
+                bn, bsc = mx.quantize_of(p["Q"], mx.AXIS_ROW, 16, m, stream)
+                a2n = torch.cat([an, an], 1).contiguous()
+                a2s = torch.cat([asc, asc], 1).contiguous()
+                mx.mxfp4_gemm(a2n, a2s, bn, bsc, p["GM"], p["GN"], 2 * p["GK"], p["C"],
+                              mx.OUT_F32, stream)
+                c = p["C"][:rows].double()
+                d = c - ref
+                nd, nr = float((d * d).sum()), float((ref * ref).sum())
+                rec[f"of_w_h16_{['ocp_floor', 'ceil'][m]}"] = {
+                    "mse": float((d * d).mean()),
+                    "cosine": float((c * ref).sum() / (c.norm() * ref.norm())),
+                    "rel_fro": (nd / nr) ** 0.5,
+                    "snr_db": 10.0 * np.log10(nr / nd)}
+                del an, asc, bn, bsc, a2n, a2s
         out[p["name"]] = rec
         del ref
     torch.cuda.synchronize()
@@ -447,6 +465,29 @@ def main():
                 quant[key]["speedup_vs_row_plus_col"] = round(
                     (quant[f"row_h16_{['ocp_floor', 'ceil'][m]}"]["us"] +
                      quant[f"col_h16_{['ocp_floor', 'ceil'][m]}"]["us"]) / (mean_ms * 1e3), 3)
+            del outs
+        # outlier fallback: q1 and the half-residual q2 in one pass (2x the output)
+        for m in (0, 1):
+            outs = [(torch.empty((R, Cc), dtype=torch.uint8, device=dev),
+                     torch.empty((R, 2 * Cc // 32), dtype=torch.uint8, device=dev))
+                    for _ in range(nsets)]
+
+            def qo(i):
+                k = i % nsets
+                mx.mxfp4_quantize_of(srcs[k], R, Cc, 0, 16, m, outs[k][0], outs[k][1], stream)
+            for i in range(10):
+                qo(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(its):
+                qo(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            mean_ms = e0.elapsed_time(e1) / its
+            b = R * Cc * (2 + 2 * (0.5 + 1 / 32))
+            quant[f"of_row_h16_{['ocp_floor', 'ceil'][m]}"] = {
+                "us": round(mean_ms * 1e3, 2), "GB/s": round(b / (mean_ms * 1e-3) / 1e9, 1),
+                "frac_hbm": round(b / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
             del outs
         if "row_h16_ocp_floor" in quant and "row_h32_ocp_floor" in quant:
             quant["h16_over_h32_row"] = round(quant["row_h16_ocp_floor"]["GB/s"] /

@@ -126,6 +126,27 @@ int mxfp4_quantize_dual(const void* src_bf16, int64_t rows, int64_t cols,
                         void* col_nibbles, void* col_e8m0, hipStream_t stream);
 
 /*
+ * mxfp4_quantize_of -- outlier-fallback (OF) operand ([P3] "three targeted
+ * fixes" section: x_OF = Q(x) + alpha Q(x - Q(x)), alpha = 0.5, which
+ * brings deadzone values back onto the grid).
+ *
+ * With y the rotated values mxfp4_quantize encodes (axis ROW or COL),
+ * q1 = Q(y) and r = fl32(y - q1): q2 = Q(fl32(r / 2)) (alpha applied as a
+ * prescale of the residual; equal to Q(r) / 2 unless the residual block's
+ * E8M0 exponent is at its floor of -127). The result is ONE packed operand
+ * twice as deep: row i of out_nibbles / out_e8m0 is q1's row followed by
+ * q2's row, i.e. out_nibbles [R][Kb] and out_e8m0 [R][2 Kb/32] with R, Kb =
+ * rows, cols (axis ROW) or cols, rows (axis COL, transposed). A GEMM of
+ * depth 2 Kb against the other operand's packed rows repeated twice along
+ * K then computes sum_k (q1 + q2) b. A block holding a non-finite rotated
+ * value is 0xFF with zero nibbles in both halves. Shapes, alignment and
+ * errors as mxfp4_quantize; axis MXFP4_AXIS_2D32 returns MXFP4_ERR_MODE.
+ */
+int mxfp4_quantize_of(const void* src_bf16, int64_t rows, int64_t cols, int axis,
+                      int hadamard, int scale_mode, void* out_nibbles, void* out_e8m0,
+                      hipStream_t stream);
+
+/*
  * mxfp4_error_stats -- tensor-level decomposition of the MXFP4 error of the
  * operand mxfp4_quantize would produce ([P3] core insight: ideal scale
  * s* = m_b / 6, e = e_scale + e_DZ + e_grid, deadzone |x| < m_b / 24;

@@ -28,7 +28,8 @@ ERROR_STATS_FIELDS = ("sum_e_scale2", "sum_e_dz2", "sum_e_grid2", "dot_scale_gri
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp4.so")
 
 EXPORTS = (
-    "mxfp4_quantize", "mxfp4_quantize_dual", "mxfp4_error_stats", "mxfp4_gemm", "mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad",
+    "mxfp4_quantize", "mxfp4_quantize_dual", "mxfp4_quantize_of", "mxfp4_error_stats",
+    "mxfp4_gemm", "mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad",
     "mxfp4_workspace_bytes", "mxfp4_status_string",
 )
 
@@ -55,6 +56,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mxfp4_quantize.restype = i32
     lib.mxfp4_quantize_dual.argtypes = [p, i64, i64, i32, i32, p, p, p, p, p]
     lib.mxfp4_quantize_dual.restype = i32
+    lib.mxfp4_quantize_of.argtypes = [p, i64, i64, i32, i32, i32, p, p, p]
+    lib.mxfp4_quantize_of.restype = i32
     lib.mxfp4_error_stats.argtypes = [p, i64, i64, i32, i32, i32, p, sz, p, p]
     lib.mxfp4_error_stats.restype = i32
     lib.mxfp4_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
@@ -132,6 +135,18 @@ def mxfp4_quantize_dual(src, rows, cols, hadamard, scale_mode, row_nibbles, row_
     _check(load_library().mxfp4_quantize_dual(
         _ptr(src), rows, cols, hadamard, scale_mode, _ptr(row_nibbles), _ptr(row_e8m0),
         _ptr(col_nibbles), _ptr(col_e8m0), _stream(stream)), "mxfp4_quantize_dual")
+
+
+def mxfp4_quantize_of(src, rows, cols, axis, hadamard, scale_mode, out_nibbles, out_e8m0,
+                      stream=None):
+    """Outlier-fallback operand (twice as deep as mxfp4_quantize's)."""
+    import torch
+    _need(src, torch.bfloat16, rows * cols, "src")
+    _need(out_nibbles, torch.uint8, rows * cols, "out_nibbles")
+    _need(out_e8m0, torch.uint8, rows * cols // 16, "out_e8m0")
+    _check(load_library().mxfp4_quantize_of(_ptr(src), rows, cols, axis, hadamard, scale_mode,
+                                            _ptr(out_nibbles), _ptr(out_e8m0), _stream(stream)),
+           "mxfp4_quantize_of")
 
 
 def mxfp4_error_stats(src, rows, cols, axis, hadamard, scale_mode, ws, out_stats, stream=None):
@@ -235,6 +250,18 @@ def quantize_dual(src, hadamard=16, scale_mode=SCALE_OCP_FLOOR, stream=None):
     out = [torch.empty(sh, dtype=torch.uint8, device=src.device) for sh in (rn, rs, cn, cs)]
     mxfp4_quantize_dual(src, rows, cols, hadamard, scale_mode, *out, stream=stream)
     return (out[0], out[1]), (out[2], out[3])
+
+
+def quantize_of(src, axis=AXIS_ROW, hadamard=16, scale_mode=SCALE_OCP_FLOOR, stream=None):
+    """Allocate and compute the OF operand; returns (nibbles [R][Kb],
+    e8m0 [R][2 Kb / 32]) with R, Kb = rows, cols (ROW) or cols, rows (COL)."""
+    import torch
+    rows, cols = src.shape
+    R, Kb = (rows, cols) if axis == AXIS_ROW else (cols, rows)
+    nib = torch.empty((R, Kb), dtype=torch.uint8, device=src.device)
+    sc = torch.empty((R, 2 * Kb // 32), dtype=torch.uint8, device=src.device)
+    mxfp4_quantize_of(src, rows, cols, axis, hadamard, scale_mode, nib, sc, stream)
+    return nib, sc
 
 
 def error_stats(src, axis=AXIS_ROW, hadamard=16, scale_mode=SCALE_OCP_FLOOR, stream=None,

@@ -17,6 +17,11 @@ hipError_t launch_quantize_dual(const void* src, int64_t rows, int64_t cols, int
                                 int scale_mode, void* rnib, void* rsc, void* cnib, void* csc,
                                 hipStream_t stream);
 
+// Outlier-fallback operand: [Q(y) | Q((y - Q(y)) / 2)] per output row,
+// 2x the nibble and scale bytes of launch_quantize (axis ROW or COL).
+hipError_t launch_quantize_of(const void* src, int64_t rows, int64_t cols, int axis, int hadamard,
+                              int scale_mode, void* nib, void* sc, hipStream_t stream);
+
 // Tensor-level error decomposition sums (mxfp4_error_stats): ws holds
 // kStatsMaxGroups x 10 doubles of partial sums, out receives 10 doubles.
 constexpr int kStatsMaxGroups = 1024;

@@ -389,6 +389,110 @@ __global__ __launch_bounds__(64 * NB) void quant_dual_kernel(const uint16_t* __r
         *reinterpret_cast<const uint2*>(lrs + t * 8);
 }
 
+// -------------------------------------------------- outlier fallback (OF)
+// [P3] "three targeted fixes" section, OF: x_OF = Q(x) + alpha Q(x - Q(x)),
+// alpha = 1/2, here applied as a prescale of the residual, Q(r / 2) (equal to
+// Q(r) / 2 unless the residual block sits at the E8M0 floor). Per 32-block:
+// quantize, decode the codes back to fp32 (exact: an E2M1 value times
+// 2^E), r = y - q1 and h = r / 2 in fp32 (one rounding each), quantize h.
+// The output is one K-concatenated operand: row i = q1's row, then q2's
+// row; a GEMM of depth 2 Kb against the other operand repeated along K
+// computes sum (q1 + q2) b. A non-finite block is 0xFF in both halves.
+__device__ __forceinline__ float e2m1_value(uint32_t code) {
+  const uint32_t m = code & 7u;
+  const float v = m < 4u ? 0.5f * (float)m : (m == 4u ? 2.f : (m == 5u ? 3.f : (m == 6u ? 4.f : 6.f)));
+  return (code & 8u) ? -v : v;
+}
+
+template <int MODE>
+__device__ __forceinline__ void of_block(float (&v)[32], uint4& n1, uint32_t& s1, uint4& n2,
+                                         uint32_t& s2) {
+  encode_block<MODE>(v, n1, s1);
+  if (s1 == 255u) {
+    n2 = make_uint4(0, 0, 0, 0);
+    s2 = 255u;
+    return;
+  }
+  const float sc = scale_of_byte(s1);
+  const uint32_t w[4] = {n1.x, n1.y, n1.z, n1.w};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float q = e2m1_value((w[i >> 3] >> (4 * (i & 7))) & 0xfu) * sc;
+    const float r = v[i] - q;
+    v[i] = 0.5f * r;
+  }
+  encode_block<MODE>(v, n2, s2);
+}
+
+// Row axis: one thread per 32-block (block b of row b / ncb).
+template <int H, int MODE>
+__global__ __launch_bounds__(256) void quant_of_row_kernel(const uint4* __restrict__ src,
+                                                           int64_t nblocks, int64_t ncb,
+                                                           uint8_t* __restrict__ nib,
+                                                           uint8_t* __restrict__ sc) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  uint4 q[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) q[j] = src[b * 4 + j];
+  float v[32];
+  unpack64B(q, v);
+  hadamard32<H>(v);
+  uint4 n1, n2;
+  uint32_t s1, s2;
+  of_block<MODE>(v, n1, s1, n2, s2);
+  const int64_t row = b / ncb, cb = b % ncb;
+  uint4* out = reinterpret_cast<uint4*>(nib + row * ncb * 32);  // 2 * ncb * 16 bytes per row
+  out[cb] = n1;
+  out[ncb + cb] = n2;
+  sc[row * 2 * ncb + cb] = (uint8_t)s1;
+  sc[row * 2 * ncb + ncb + cb] = (uint8_t)s2;
+}
+
+// Column axis: one thread per (column, 32-row band); loads are 2-byte,
+// coalesced across the threads of a row. Output row c of the transposed
+// operand: the band's q1 block at band, its q2 block at nb + band.
+template <int H, int MODE>
+__global__ __launch_bounds__(256) void quant_of_col_kernel(const uint16_t* __restrict__ src,
+                                                           int64_t rows, int64_t cols,
+                                                           uint8_t* __restrict__ nib,
+                                                           uint8_t* __restrict__ sc) {
+  const int64_t ncg = (cols + 255) / 256;
+  const int64_t c = ((int64_t)blockIdx.x % ncg) * 256 + threadIdx.x;
+  const int64_t band = (int64_t)blockIdx.x / ncg;
+  if (c >= cols || band * 32 >= rows) return;
+  float v[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) v[r] = __uint_as_float((uint32_t)src[(band * 32 + r) * cols + c] << 16);
+  hadamard32<H>(v);
+  uint4 n1, n2;
+  uint32_t s1, s2;
+  of_block<MODE>(v, n1, s1, n2, s2);
+  const int64_t nb = rows / 32;
+  uint4* out = reinterpret_cast<uint4*>(nib + c * nb * 32);
+  out[band] = n1;
+  out[nb + band] = n2;
+  sc[c * 2 * nb + band] = (uint8_t)s1;
+  sc[c * 2 * nb + nb + band] = (uint8_t)s2;
+}
+
+template <int H, int MODE>
+hipError_t dispatch_of(const void* src, int64_t rows, int64_t cols, int axis, void* nib, void* sc,
+                       hipStream_t st) {
+  if (axis == 0) {
+    const int64_t ncb = cols / 32, nblocks = rows * ncb;
+    hipLaunchKernelGGL((quant_of_row_kernel<H, MODE>), dim3((unsigned)((nblocks + 255) / 256)),
+                       dim3(256), 0, st, static_cast<const uint4*>(src), nblocks, ncb,
+                       static_cast<uint8_t*>(nib), static_cast<uint8_t*>(sc));
+  } else {
+    const int64_t grid = (rows / 32) * ((cols + 255) / 256);
+    hipLaunchKernelGGL((quant_of_col_kernel<H, MODE>), dim3((unsigned)grid), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(src), rows, cols, static_cast<uint8_t*>(nib),
+                       static_cast<uint8_t*>(sc));
+  }
+  return hipGetLastError();
+}
+
 template <int H, int MODE>
 hipError_t dispatch_axis(const void* src, int64_t rows, int64_t cols, int axis, void* nib,
                          void* sc, hipStream_t st) {
@@ -481,6 +585,19 @@ hipError_t launch_quantize_dual(const void* src, int64_t rows, int64_t cols, int
                          : dispatch_dual<32, kOcpFloor>(src, rows, cols, rnib, rsc, cnib, csc, stream);
     default: return ceil ? dispatch_dual<0, kCeil>(src, rows, cols, rnib, rsc, cnib, csc, stream)
                          : dispatch_dual<0, kOcpFloor>(src, rows, cols, rnib, rsc, cnib, csc, stream);
+  }
+}
+
+hipError_t launch_quantize_of(const void* src, int64_t rows, int64_t cols, int axis, int hadamard,
+                              int scale_mode, void* nib, void* sc, hipStream_t stream) {
+  const bool ceil = scale_mode == kCeil;
+  switch (hadamard) {
+    case 16: return ceil ? dispatch_of<16, kCeil>(src, rows, cols, axis, nib, sc, stream)
+                         : dispatch_of<16, kOcpFloor>(src, rows, cols, axis, nib, sc, stream);
+    case 32: return ceil ? dispatch_of<32, kCeil>(src, rows, cols, axis, nib, sc, stream)
+                         : dispatch_of<32, kOcpFloor>(src, rows, cols, axis, nib, sc, stream);
+    default: return ceil ? dispatch_of<0, kCeil>(src, rows, cols, axis, nib, sc, stream)
+                         : dispatch_of<0, kOcpFloor>(src, rows, cols, axis, nib, sc, stream);
   }
 }
 

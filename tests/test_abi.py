@@ -128,6 +128,21 @@ def test_quantize_dual_validation(lib):
     assert qd(lib, cols=0, src=NULL, rn=NULL, rs=NULL, cn=NULL, cs=NULL) == 0
 
 
+def test_quantize_of_validation(lib):
+    call = lambda **kw: lib.mxfp4_quantize_of(kw.get("src", FAKE), kw.get("rows", 64),
+                                              kw.get("cols", 64), kw.get("axis", 0),
+                                              kw.get("h", 16), kw.get("mode", 0),
+                                              kw.get("nib", FAKE), kw.get("sc", FAKE), NULL)
+    assert call(axis=2) == 3
+    assert call(h=4) == 3
+    assert call(mode=3) == 3
+    assert call(cols=40) == 2
+    assert call(axis=1, rows=40) == 2
+    assert call(nib=NULL) == 1
+    assert call(src=FAKE_ODD) == 6
+    assert call(rows=0, src=NULL, nib=NULL, sc=NULL) == 0
+
+
 def es(lib, src=FAKE, rows=64, cols=64, axis=0, h=16, mode=0, ws=FAKE, wsb=None, out=FAKE):
     wsb = mx.ERROR_STATS_WS_BYTES if wsb is None else wsb
     return lib.mxfp4_error_stats(src, rows, cols, axis, h, mode, ws, wsb, out, NULL)
