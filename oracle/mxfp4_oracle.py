@@ -262,6 +262,64 @@ def quantize_of(src_bf16: np.ndarray, axis: int, hadamard: int, mode: int):
 
 
 # --------------------------------------------------------------------------
+# Macro-block scaling ([P3] "three targeted fixes" section, MBS: an 8-bit
+# mantissa (1 + m) per macro-block of B_M = 128 elements, used as
+# x_hat = Q((1 + m) x) / (1 + m))
+# --------------------------------------------------------------------------
+MBS_BLOCK = 128
+
+
+def mbs_mantissa(M: np.ndarray) -> np.ndarray:
+    """8-bit mantissa byte m of macro-blocks with absolute maximum ``M``.
+
+    Reading of the pages (which fix the form, not the rule): c = 1 + m/256
+    is the largest such factor with c M <= 6 2^k, k the smallest integer
+    with 6 2^k >= M, so the prescaled macro maximum sits at the top of its
+    E8M0 bracket: m = floor(256 (6 2^k / M - 1)), evaluated in fp64.
+    M == 0 or non-finite gives m = 0.
+    """
+    Md = np.asarray(M, dtype=np.float64)
+    ok = np.isfinite(Md) & (Md > 0)
+    safe = np.where(ok, Md, 1.0)
+    frac, e1 = np.frexp(safe)                  # safe = frac 2^e1, frac in [0.5, 1)
+    f, e = 2.0 * frac, e1.astype(np.int64) - 1
+    k = np.where(f <= 1.5, e - 2, e - 1)
+    c = np.ldexp(6.0, k) / safe
+    m = np.floor((c - 1.0) * 256.0)
+    return np.where(ok, np.clip(m, 0, 255), 0).astype(np.uint8)
+
+
+def quantize_mbs(src_bf16: np.ndarray, axis: int, hadamard: int, mode: int):
+    """MBS operand: (nibbles, scales, mbs) with mbs [R][Kb/128] the mantissa
+    bytes; nibbles and E8M0 scales are this module's quantizer applied to
+    fl32(c y), c = 1 + m/256 of y's macro-block (y the rotated values, row or
+    col axis, Kb % 128 == 0). Dequantize with ``dequantize_mbs``."""
+    x = bf16_to_f32(src_bf16)
+    if axis == AXIS_COL:
+        x = np.ascontiguousarray(x.T)
+    elif axis != AXIS_ROW:
+        raise ValueError("MBS is defined here for 1x32 and 32x1 blocks")
+    if x.shape[1] % MBS_BLOCK:
+        raise ValueError("blocked axis must be a multiple of 128")
+    y = hadamard_rotate(x, hadamard)
+    r, kb = y.shape
+    yb = y.reshape(r, kb // MBS_BLOCK, MBS_BLOCK)
+    with np.errstate(invalid="ignore"):
+        M = np.max(np.abs(yb), axis=2)
+    m = mbs_mantissa(M)
+    c = (1.0 + m.astype(np.float32) / np.float32(256)).astype(np.float32)
+    yp = (yb * c[:, :, None]).astype(np.float32).reshape(r, kb)
+    nib, sc = _quantize_rows(yp, mode)
+    return nib, sc, m
+
+
+def dequantize_mbs(nib: np.ndarray, sc: np.ndarray, mbs: np.ndarray) -> np.ndarray:
+    """fp64 values Q(c y) / c of an MBS operand."""
+    c = 1.0 + np.asarray(mbs, dtype=np.float64) / 256.0
+    return dequantize(nib, sc) / np.repeat(c, MBS_BLOCK, axis=1)
+
+
+# --------------------------------------------------------------------------
 # Reconstruction ([P1] quick-read block: x_rec = 2^E * Q_FP4(x / 2^E))
 # --------------------------------------------------------------------------
 def dequantize(nib: np.ndarray, sc: np.ndarray, two_d: bool = False) -> np.ndarray:

@@ -563,6 +563,70 @@ def test_of_reduces_the_error_and_keeps_nonfinite_blocks():
     assert np.all(n[5, 32:48] == 0) and np.all(n[5, 256 + 32:256 + 48] == 0)
 
 
+# ---------------------------------------------------- macro-block scaling
+def test_mbs_mantissa_against_exact_search():
+    """m = the largest j in [0, 255] with (1 + j/256) M <= 6 2^k, k the
+    smallest integer with 6 2^k >= M: exact rational search over bf16-like
+    and random fp32 maxima (the rule is a reading; this pins its arithmetic)."""
+    rng = np.random.default_rng(12)
+    Ms = np.concatenate([rng.lognormal(0, 3, 3000).astype(np.float32),
+                         np.float32([6.0, 5.0, 3.0, 1.5, 0.75, 6.0 * 2.0 ** -20, 1e-30, 3e30])])
+    got = O.mbs_mantissa(Ms)
+    for M, m in zip(Ms, got):
+        F = Fraction(float(M))
+        k = -200
+        while 6 * Fraction(2) ** k < F:
+            k += 1
+        best = max(j for j in range(256) if (1 + Fraction(j, 256)) * F <= 6 * Fraction(2) ** k)
+        assert m == best, (float(M), int(m), best)
+    assert list(O.mbs_mantissa(np.float32([0.0, np.inf, np.nan]))) == [0, 0, 0]
+
+
+def test_mbs_hand_worked_block():
+    """Macro max 5: k = 0, c = 1 + floor(256 * 0.2) / 256 = 1 + 51/256; 5 c =
+    5.996 -> E = 0, code 6.0 -> 6 / c = 1536/307 (plain ceil: 5 -> 4, the tie
+    rounds to the even code). bf16(0.3) = 0.30078125 -> c x = 0.3607 -> 0.5 ->
+    0.5 / c. A block of max 6 needs no correction: m = 0, plain operand."""
+    blk = np.zeros((1, 128), dtype=np.float64)
+    blk[0, 0], blk[0, 1] = 5.0, 0.3
+    src = synthetic.f64_to_bf16_bits(blk)
+    n, s, m = O.quantize_mbs(src, O.AXIS_ROW, 0, O.MODE_CEIL)
+    assert m[0, 0] == 51 and s[0, 0] == 127
+    d = O.dequantize_mbs(n, s, m)
+    c = 1 + 51 / 256
+    assert d[0, 0] == 6.0 / c and d[0, 1] == 0.5 / c
+    assert O.dequantize(*O.quantize(src, O.AXIS_ROW, 0, O.MODE_CEIL))[0, 0] == 4.0
+    blk[0, 0] = 6.0
+    src = synthetic.f64_to_bf16_bits(blk)
+    n, s, m = O.quantize_mbs(src, O.AXIS_ROW, 0, O.MODE_CEIL)
+    n0, s0 = O.quantize(src, O.AXIS_ROW, 0, O.MODE_CEIL)
+    assert m[0, 0] == 0 and np.array_equal(n, n0) and np.array_equal(s, s0)
+
+
+@pytest.mark.parametrize("mode", [O.MODE_OCP_FLOOR, O.MODE_CEIL])
+def test_mbs_removes_the_scale_bias_of_the_macro_max_block(mode):
+    """After the prescale the macro maximum's block has gamma = 2^E / s* in
+    [1, 1 + 2^-7) (E8M0 over the ideal scale of the prescaled block), in both
+    rules; without MBS gamma spreads over [1, 2). The operand is also
+    dequantized through a different path (dequantize / c)."""
+    src = _stat_src(256, 1024, 8)
+    n, s, m = O.quantize_mbs(src, O.AXIS_ROW, 16, mode)
+    y = O.hadamard_rotate(O.bf16_to_f32(src), 16)
+    yb = y.reshape(256, 8, 128)
+    c = (1 + m.astype(np.float64) / 256)
+    M = np.max(np.abs(yb), axis=2).astype(np.float64)
+    blk = np.argmax(np.abs(yb), axis=2) // 32
+    E = s.reshape(256, 8, 4)[np.arange(256)[:, None], np.arange(8)[None, :], blk].astype(np.int64) - 127
+    cM = (yb.astype(np.float32) * c[:, :, None].astype(np.float32)).astype(np.float32)
+    cM = np.max(np.abs(cM), axis=2).astype(np.float64)
+    gamma = np.ldexp(1.0, E) / (cM / 6)
+    assert np.all(gamma >= 1.0) and np.all(gamma < 1 + 2 ** -7)
+    g0 = np.ldexp(1.0, O.e8m0_exponent(M.astype(np.float32), O.MODE_CEIL)) / (M / 6)
+    assert g0.max() > 1.5
+    d = O.dequantize_mbs(n, s, m)
+    assert np.allclose(d * np.repeat(c, 128, axis=1), O.dequantize(n, s), rtol=1e-15, atol=0)
+
+
 # ------------------------------------------------------- hand-worked blocks
 def test_hand_worked_blocks():
     """Blocks whose encodings follow from the definitions by hand."""
