@@ -489,6 +489,30 @@ def main():
                 "us": round(mean_ms * 1e3, 2), "GB/s": round(b / (mean_ms * 1e-3) / 1e9, 1),
                 "frac_hbm": round(b / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
             del outs
+        # macro-block scaling: prescaled operand + one mantissa byte per 128
+        for ax in (0, 1):
+            ns_, ss_ = mx.packed_shapes(R, Cc, ax)
+            ms_ = (R, Cc // 128) if ax == 0 else (Cc, R // 128)
+            outs = [[torch.empty(sh, dtype=torch.uint8, device=dev) for sh in (ns_, ss_, ms_)]
+                    for _ in range(nsets)]
+
+            def qm(i):
+                k = i % nsets
+                mx.mxfp4_quantize_mbs(srcs[k], R, Cc, ax, 16, 1, *outs[k], stream=stream)
+            for i in range(10):
+                qm(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(its):
+                qm(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            mean_ms = e0.elapsed_time(e1) / its
+            b = R * Cc * (2 + 0.5 + 1 / 32 + 1 / 128)
+            quant[f"mbs_{['row', 'col'][ax]}_h16_ceil"] = {
+                "us": round(mean_ms * 1e3, 2), "GB/s": round(b / (mean_ms * 1e-3) / 1e9, 1),
+                "frac_hbm": round(b / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            del outs
         if "row_h16_ocp_floor" in quant and "row_h32_ocp_floor" in quant:
             quant["h16_over_h32_row"] = round(quant["row_h16_ocp_floor"]["GB/s"] /
                                               quant["row_h32_ocp_floor"]["GB/s"], 3)

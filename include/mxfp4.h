@@ -147,6 +147,27 @@ int mxfp4_quantize_of(const void* src_bf16, int64_t rows, int64_t cols, int axis
                       hipStream_t stream);
 
 /*
+ * mxfp4_quantize_mbs -- macro-block-scaled (MBS) operand ([P3] "three
+ * targeted fixes" section: an 8-bit mantissa correction s = 2^e (1 + m)
+ * per macro-block of 128 elements, x_hat = Q((1 + m) x) / (1 + m)).
+ *
+ * With y the rotated values mxfp4_quantize encodes (axis ROW or COL) and
+ * M the absolute maximum of each run of 128 along the blocked axis:
+ * c = 1 + m/256 with m the largest byte such that c M <= 6 2^k, k the
+ * smallest integer with 6 2^k >= M (m = floor(256 (6 2^k / M - 1)) in
+ * fp64; 0 for a zero or non-finite M). out_nibbles / out_e8m0 receive
+ * exactly mxfp4_quantize's output for fl32(c y); out_mbs receives m,
+ * [rows][cols/128] (ROW) or [cols][rows/128] (COL). The value is
+ * dequant(nibbles, e8m0) / c; a GEMM consuming it needs that per-128-k
+ * factor on each operand (not provided by mxfp4_gemm). The blocked axis
+ * must be a multiple of 128; otherwise as mxfp4_quantize (axis 2D32 returns
+ * MXFP4_ERR_MODE).
+ */
+int mxfp4_quantize_mbs(const void* src_bf16, int64_t rows, int64_t cols, int axis,
+                       int hadamard, int scale_mode, void* out_nibbles, void* out_e8m0,
+                       void* out_mbs, hipStream_t stream);
+
+/*
  * mxfp4_error_stats -- tensor-level decomposition of the MXFP4 error of the
  * operand mxfp4_quantize would produce ([P3] core insight: ideal scale
  * s* = m_b / 6, e = e_scale + e_DZ + e_grid, deadzone |x| < m_b / 24;

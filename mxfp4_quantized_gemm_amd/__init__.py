@@ -28,8 +28,8 @@ ERROR_STATS_FIELDS = ("sum_e_scale2", "sum_e_dz2", "sum_e_grid2", "dot_scale_gri
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp4.so")
 
 EXPORTS = (
-    "mxfp4_quantize", "mxfp4_quantize_dual", "mxfp4_quantize_of", "mxfp4_error_stats",
-    "mxfp4_gemm", "mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad",
+    "mxfp4_quantize", "mxfp4_quantize_dual", "mxfp4_quantize_of", "mxfp4_quantize_mbs",
+    "mxfp4_error_stats", "mxfp4_gemm", "mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad",
     "mxfp4_workspace_bytes", "mxfp4_status_string",
 )
 
@@ -58,6 +58,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mxfp4_quantize_dual.restype = i32
     lib.mxfp4_quantize_of.argtypes = [p, i64, i64, i32, i32, i32, p, p, p]
     lib.mxfp4_quantize_of.restype = i32
+    lib.mxfp4_quantize_mbs.argtypes = [p, i64, i64, i32, i32, i32, p, p, p, p]
+    lib.mxfp4_quantize_mbs.restype = i32
     lib.mxfp4_error_stats.argtypes = [p, i64, i64, i32, i32, i32, p, sz, p, p]
     lib.mxfp4_error_stats.restype = i32
     lib.mxfp4_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
@@ -147,6 +149,20 @@ def mxfp4_quantize_of(src, rows, cols, axis, hadamard, scale_mode, out_nibbles, 
     _check(load_library().mxfp4_quantize_of(_ptr(src), rows, cols, axis, hadamard, scale_mode,
                                             _ptr(out_nibbles), _ptr(out_e8m0), _stream(stream)),
            "mxfp4_quantize_of")
+
+
+def mxfp4_quantize_mbs(src, rows, cols, axis, hadamard, scale_mode, out_nibbles, out_e8m0,
+                       out_mbs, stream=None):
+    """Macro-block-scaled operand: nibbles and E8M0 of the prescaled values
+    plus one mantissa byte per 128 elements."""
+    import torch
+    _need(src, torch.bfloat16, rows * cols, "src")
+    _need(out_nibbles, torch.uint8, rows * cols // 2, "out_nibbles")
+    _need(out_e8m0, torch.uint8, rows * cols // 32, "out_e8m0")
+    _need(out_mbs, torch.uint8, rows * cols // 128, "out_mbs")
+    _check(load_library().mxfp4_quantize_mbs(_ptr(src), rows, cols, axis, hadamard, scale_mode,
+                                             _ptr(out_nibbles), _ptr(out_e8m0), _ptr(out_mbs),
+                                             _stream(stream)), "mxfp4_quantize_mbs")
 
 
 def mxfp4_error_stats(src, rows, cols, axis, hadamard, scale_mode, ws, out_stats, stream=None):
@@ -262,6 +278,17 @@ def quantize_of(src, axis=AXIS_ROW, hadamard=16, scale_mode=SCALE_OCP_FLOOR, str
     sc = torch.empty((R, 2 * Kb // 32), dtype=torch.uint8, device=src.device)
     mxfp4_quantize_of(src, rows, cols, axis, hadamard, scale_mode, nib, sc, stream)
     return nib, sc
+
+
+def quantize_mbs(src, axis=AXIS_ROW, hadamard=16, scale_mode=SCALE_CEIL, stream=None):
+    """Allocate and compute the MBS operand; returns (nibbles, e8m0, mbs)."""
+    import torch
+    rows, cols = src.shape
+    ns, ss = packed_shapes(rows, cols, axis)
+    ms = (rows, cols // 128) if axis == AXIS_ROW else (cols, rows // 128)
+    out = [torch.empty(sh, dtype=torch.uint8, device=src.device) for sh in (ns, ss, ms)]
+    mxfp4_quantize_mbs(src, rows, cols, axis, hadamard, scale_mode, *out, stream=stream)
+    return tuple(out)
 
 
 def error_stats(src, axis=AXIS_ROW, hadamard=16, scale_mode=SCALE_OCP_FLOOR, stream=None,

@@ -166,6 +166,20 @@ int mxfp4_quantize_of(const void* src_bf16, int64_t rows, int64_t cols, int axis
                                            out_nibbles, out_e8m0, stream));
 }
 
+int mxfp4_quantize_mbs(const void* src_bf16, int64_t rows, int64_t cols, int axis, int hadamard,
+                       int scale_mode, void* out_nibbles, void* out_e8m0, void* out_mbs,
+                       hipStream_t stream) {
+  if (axis != MXFP4_AXIS_ROW && axis != MXFP4_AXIS_COL) return MXFP4_ERR_MODE;
+  const int st = check_quantize(src_bf16, rows, cols, axis, hadamard, scale_mode, out_nibbles,
+                                out_e8m0);
+  if (st != MXFP4_OK) return st;
+  if ((axis == MXFP4_AXIS_ROW ? cols : rows) % 128) return MXFP4_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return MXFP4_OK;
+  if (!out_mbs) return MXFP4_ERR_NULL;
+  return hip_status(mx::launch_quantize_mbs(src_bf16, rows, cols, axis, hadamard, scale_mode,
+                                            out_nibbles, out_e8m0, out_mbs, stream));
+}
+
 int mxfp4_error_stats(const void* src_bf16, int64_t rows, int64_t cols, int axis, int hadamard,
                       int scale_mode, void* ws, size_t ws_bytes, double* out_stats,
                       hipStream_t stream) {

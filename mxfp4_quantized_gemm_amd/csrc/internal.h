@@ -22,6 +22,12 @@ hipError_t launch_quantize_dual(const void* src, int64_t rows, int64_t cols, int
 hipError_t launch_quantize_of(const void* src, int64_t rows, int64_t cols, int axis, int hadamard,
                               int scale_mode, void* nib, void* sc, hipStream_t stream);
 
+// Macro-block-scaled operand: launch_quantize of fl32(c y) plus one mantissa
+// byte per 128 elements along the blocked axis (axis ROW or COL).
+hipError_t launch_quantize_mbs(const void* src, int64_t rows, int64_t cols, int axis,
+                               int hadamard, int scale_mode, void* nib, void* sc, void* mbs,
+                               hipStream_t stream);
+
 // Tensor-level error decomposition sums (mxfp4_error_stats): ws holds
 // kStatsMaxGroups x 10 doubles of partial sums, out receives 10 doubles.
 constexpr int kStatsMaxGroups = 1024;

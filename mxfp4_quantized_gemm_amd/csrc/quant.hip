@@ -493,6 +493,117 @@ hipError_t dispatch_of(const void* src, int64_t rows, int64_t cols, int axis, vo
   return hipGetLastError();
 }
 
+// ---------------------------------------------- macro-block scaling (MBS)
+// [P3] "three targeted fixes" section, MBS: one 8-bit mantissa (1 + m) per
+// macro-block of 128 elements (4 blocks), x_hat = Q((1 + m) x) / (1 + m).
+// m is chosen (a reading; the pages fix only the form) as the largest byte
+// with (1 + m/256) M <= 6 2^k, M the macro-block amax and k the smallest
+// integer with 6 2^k >= M: the prescaled macro maximum then sits at the top
+// of its E8M0 bracket, removing that block's scale bias. Evaluated in fp64:
+// m = floor(256 (6 2^k / M - 1)); zero or non-finite M gives m = 0.
+__device__ __forceinline__ uint32_t mbs_byte(uint32_t am) {
+  if (am == 0u || am >= 0x7f800000u) return 0u;
+  const double M = (double)__uint_as_float(am);
+  int e1;
+  const double fr = frexp(M, &e1);  // M = fr 2^e1, fr in [0.5, 1)
+  const int e = e1 - 1;
+  const int k = (2.0 * fr <= 1.5) ? e - 2 : e - 1;
+  const double c = ldexp(6.0, k) / M;
+  const double m = floor((c - 1.0) * 256.0);
+  return (uint32_t)(m < 0.0 ? 0.0 : (m > 255.0 ? 255.0 : m));
+}
+
+// Row axis: one thread per 32-block; the four lanes of a quad hold the four
+// blocks of one macro-block (rows are a multiple of 128 long) and share
+// their amax through DPP.
+template <int H, int MODE>
+__global__ __launch_bounds__(256) void quant_mbs_row_kernel(const uint4* __restrict__ src,
+                                                            int64_t nblocks,
+                                                            uint4* __restrict__ nib,
+                                                            uint8_t* __restrict__ sc,
+                                                            uint8_t* __restrict__ mbs) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblocks) return;  // nblocks % 4 == 0: whole quads leave together
+  uint4 q[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) q[j] = src[b * 4 + j];
+  float v[32];
+  unpack64B(q, v);
+  hadamard32<H>(v);
+  uint32_t am = amax_bits32(v);
+  am = max(am, xchg<1>(am));
+  am = max(am, xchg<2>(am));
+  const uint32_t m = mbs_byte(am);
+  const float c = 1.0f + (float)m * 0.00390625f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = c * v[i];
+  uint4 out;
+  uint32_t s;
+  encode_block<MODE>(v, out, s);
+  nib[b] = out;
+  sc[b] = (uint8_t)s;
+  if ((b & 3) == 0) mbs[b >> 2] = (uint8_t)m;
+}
+
+// Column axis: one thread per (column, 128-row macro band); a first pass
+// takes the amax of the four rotated 32x1 blocks, a second reloads,
+// rotates, prescales and encodes them (2-byte loads, coalesced across the
+// threads of a row).
+template <int H, int MODE>
+__global__ __launch_bounds__(256) void quant_mbs_col_kernel(const uint16_t* __restrict__ src,
+                                                            int64_t rows, int64_t cols,
+                                                            uint8_t* __restrict__ nib,
+                                                            uint8_t* __restrict__ sc,
+                                                            uint8_t* __restrict__ mbs) {
+  const int64_t ncg = (cols + 255) / 256;
+  const int64_t c = ((int64_t)blockIdx.x % ncg) * 256 + threadIdx.x;
+  const int64_t mb = (int64_t)blockIdx.x / ncg;
+  if (c >= cols) return;
+  const uint16_t* p = src + mb * 128 * cols + c;
+  uint32_t am = 0;
+  for (int j = 0; j < 4; ++j) {
+    float v[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) v[r] = __uint_as_float((uint32_t)p[(32 * j + r) * cols] << 16);
+    hadamard32<H>(v);
+    am = max(am, amax_bits32(v));
+  }
+  const uint32_t m = mbs_byte(am);
+  const float cf = 1.0f + (float)m * 0.00390625f;
+  for (int j = 0; j < 4; ++j) {
+    float v[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) v[r] = __uint_as_float((uint32_t)p[(32 * j + r) * cols] << 16);
+    hadamard32<H>(v);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = cf * v[i];
+    uint4 out;
+    uint32_t s;
+    encode_block<MODE>(v, out, s);
+    *reinterpret_cast<uint4*>(nib + c * (rows / 2) + (4 * mb + j) * 16) = out;
+    sc[c * (rows / 32) + 4 * mb + j] = (uint8_t)s;
+  }
+  mbs[c * (rows / 128) + mb] = (uint8_t)m;
+}
+
+template <int H, int MODE>
+hipError_t dispatch_mbs(const void* src, int64_t rows, int64_t cols, int axis, void* nib,
+                        void* sc, void* mbs, hipStream_t st) {
+  if (axis == 0) {
+    const int64_t nblocks = rows * (cols / 32);
+    hipLaunchKernelGGL((quant_mbs_row_kernel<H, MODE>), dim3((unsigned)((nblocks + 255) / 256)),
+                       dim3(256), 0, st, static_cast<const uint4*>(src), nblocks,
+                       static_cast<uint4*>(nib), static_cast<uint8_t*>(sc),
+                       static_cast<uint8_t*>(mbs));
+  } else {
+    const int64_t grid = (rows / 128) * ((cols + 255) / 256);
+    hipLaunchKernelGGL((quant_mbs_col_kernel<H, MODE>), dim3((unsigned)grid), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(src), rows, cols, static_cast<uint8_t*>(nib),
+                       static_cast<uint8_t*>(sc), static_cast<uint8_t*>(mbs));
+  }
+  return hipGetLastError();
+}
+
 template <int H, int MODE>
 hipError_t dispatch_axis(const void* src, int64_t rows, int64_t cols, int axis, void* nib,
                          void* sc, hipStream_t st) {
@@ -598,6 +709,20 @@ hipError_t launch_quantize_of(const void* src, int64_t rows, int64_t cols, int a
                          : dispatch_of<32, kOcpFloor>(src, rows, cols, axis, nib, sc, stream);
     default: return ceil ? dispatch_of<0, kCeil>(src, rows, cols, axis, nib, sc, stream)
                          : dispatch_of<0, kOcpFloor>(src, rows, cols, axis, nib, sc, stream);
+  }
+}
+
+hipError_t launch_quantize_mbs(const void* src, int64_t rows, int64_t cols, int axis,
+                               int hadamard, int scale_mode, void* nib, void* sc, void* mbs,
+                               hipStream_t stream) {
+  const bool ceil = scale_mode == kCeil;
+  switch (hadamard) {
+    case 16: return ceil ? dispatch_mbs<16, kCeil>(src, rows, cols, axis, nib, sc, mbs, stream)
+                         : dispatch_mbs<16, kOcpFloor>(src, rows, cols, axis, nib, sc, mbs, stream);
+    case 32: return ceil ? dispatch_mbs<32, kCeil>(src, rows, cols, axis, nib, sc, mbs, stream)
+                         : dispatch_mbs<32, kOcpFloor>(src, rows, cols, axis, nib, sc, mbs, stream);
+    default: return ceil ? dispatch_mbs<0, kCeil>(src, rows, cols, axis, nib, sc, mbs, stream)
+                         : dispatch_mbs<0, kOcpFloor>(src, rows, cols, axis, nib, sc, mbs, stream);
   }
 }
 

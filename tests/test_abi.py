@@ -143,6 +143,21 @@ def test_quantize_of_validation(lib):
     assert call(rows=0, src=NULL, nib=NULL, sc=NULL) == 0
 
 
+def test_quantize_mbs_validation(lib):
+    call = lambda **kw: lib.mxfp4_quantize_mbs(kw.get("src", FAKE), kw.get("rows", 128),
+                                               kw.get("cols", 128), kw.get("axis", 0),
+                                               kw.get("h", 16), kw.get("mode", 1),
+                                               kw.get("nib", FAKE), kw.get("sc", FAKE),
+                                               kw.get("mbs", FAKE), NULL)
+    assert call(axis=2) == 3
+    assert call(cols=96) == 2                  # row axis: cols % 128
+    assert call(axis=1, rows=96) == 2          # col axis: rows % 128
+    assert call(mbs=NULL) == 1
+    assert call(nib=NULL) == 1
+    assert call(src=FAKE_ODD) == 6
+    assert call(rows=0, src=NULL, nib=NULL, sc=NULL, mbs=NULL) == 0
+
+
 def es(lib, src=FAKE, rows=64, cols=64, axis=0, h=16, mode=0, ws=FAKE, wsb=None, out=FAKE):
     wsb = mx.ERROR_STATS_WS_BYTES if wsb is None else wsb
     return lib.mxfp4_error_stats(src, rows, cols, axis, h, mode, ws, wsb, out, NULL)
