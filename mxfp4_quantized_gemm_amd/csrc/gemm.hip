@@ -238,10 +238,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
 // operand), so a lane's accumulator registers 4q..4q+3 hold four
 // consecutive columns of one C row: the epilogue writes 16-byte vectors.
 //
-// LDS tile rows are KB bytes of 16-byte chunks; chunk c of row r is stored
-// at c ^ g(r), which spreads the rows read together by one ds_read_b128
-// over distinct banks for both 8- and 16-lane service groups:
-// g(r) = ((r >> 1) ^ (r >> 3)) & 3 for 4 chunks, (r ^ (r >> 3)) & 7 for 8.
+// LDS tiles are fragment-major: for each group of 32 rows, chunk column c
+// (the rows' 16-byte chunks c) is 512 contiguous bytes padded to 544 (576 for
+// 64-byte k-tiles). An MFMA fragment read is then 32 lanes x 16 contiguous
+// bytes per half-wave and the staging writes are 16 lanes x 16 contiguous
+// bytes; with the padding both run near the LDS peak (measured 188 and 245
+// B/clk per CU, where row-major 16-byte writes ran at 76).
 namespace lt {
 
 // Output tiles are walked in groups of GROUP_M tile-rows (see tile_of).
@@ -251,14 +253,6 @@ constexpr int GROUP_M = 4;
 // whose copies lower to memcpy, which keeps the struct in scratch memory.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-// Swizzle of the 16-byte chunks of an LDS row. It depends on row bits 0-4
-// only: every row a lane touches is congruent to the lane's row modulo 32,
-// so the swizzle is a per-lane constant and tile offsets become immediates.
-template <int KB>
-__device__ __forceinline__ int swz(int r) {
-  return KB == 64 ? (((r >> 1) ^ (r >> 3)) & 3) : ((r & 7) ^ ((r >> 3) & 3));
-}
 
 // Work-group barrier that orders LDS only: global loads in flight (the
 // prefetch of later k-tiles) stay in flight across it.
@@ -375,9 +369,8 @@ __device__ __forceinline__ void tile_of(int64_t wg, int64_t nwg, int64_t ntm, in
 // 2 x 4) computes a 256 x 256 tile of C, each wave 128 x 64 (4 x 2 MFMA
 // tiles, 128 fp32 accumulators per lane, in AGPRs). k-tiles are KB = 128
 // (256-deep) or 64 (128-deep) bytes of every operand row; A and B rows are
-// staged in LDS as rows of KB bytes with a lane-constant 16-byte-chunk
-// swizzle, double-buffered, loaded through buffer resources into staging
-// registers. Within a k-tile:
+// staged in LDS in the fragment-major layout above, double-buffered, loaded
+// through buffer resources into staging registers. Within a k-tile:
 //  * scale bytes are stored in LDS pre-split into an "even blocks" word and
 //    an "odd blocks" word per row, laid out so that a lane's TM (TN) rows are
 //    consecutive: one vector LDS read per operand per k-tile, and byte s of
@@ -401,7 +394,11 @@ struct Cfg {
   static constexpr int CPR = KB / 16;                    // 16-byte chunks per row
   static constexpr int SB = KB / 16;                     // scale bytes per row per k-tile
   static constexpr int KSTEPS = KB / 32;                 // MFMA k-steps (64 elements each)
-  static constexpr int TA = BM * KB, TB = BN * KB;
+  // Fragment-major tiles: per group of 32 rows, chunk column c holds the 32
+  // rows' 16-byte chunk c back to back, padded to CP bytes.
+  static constexpr int CP = KB == 128 ? 544 : 576;       // chunk-column pitch
+  static constexpr int GP = (KB / 16) * CP;              // 32-row group pitch
+  static constexpr int TA = (BM / 32) * GP, TB = (BN / 32) * GP;
   static constexpr int SOFF = TA + TB;                   // A scale words, then B scale words
   static constexpr int SBOFF = SOFF + BM * 8;
   static constexpr int TRASH = SBOFF + BN * 8;           // sink for surplus scale rows
@@ -446,19 +443,21 @@ __device__ __forceinline__ void make_spos(SPos<G, TM, TN>& P, int t) {
 }
 
 // Part P of NP of the staging registers -> LDS stage st (chunks in the
-// swizzled row layout; the scale words go with the last part).
+// fragment-major layout; the scale words go with the last part). Thread t
+// holds chunk c = t % CPR of rows r0 + RSTEP i: group (r0 >> 5) + i RSTEP/32,
+// slot r0 & 31 of chunk column c.
 template <class G, int TM, int TN, int P, int NP>
 __device__ __forceinline__ void lstore_part(const Regs<G>& R, const SPos<G, TM, TN>& SP,
                                             uint8_t* st, int t) {
-  constexpr int KB = G::CPR * 16;
   const int r0 = t / G::CPR, c = t % G::CPR;
-  uint8_t* pa = st + r0 * KB + ((c ^ swz<KB>(r0 & 31)) << 4);
+  uint8_t* pa = st + (r0 >> 5) * G::GP + c * G::CP + (r0 & 31) * 16;
+  constexpr int STEP = (G::RSTEP / 32) * G::GP;
 #pragma unroll
   for (int i = G::CA * P / NP; i < G::CA * (P + 1) / NP; ++i)
-    *reinterpret_cast<u32x4*>(pa + i * G::RSTEP * KB) = R.a[i];
+    *reinterpret_cast<u32x4*>(pa + i * STEP) = R.a[i];
 #pragma unroll
   for (int i = G::CB * P / NP; i < G::CB * (P + 1) / NP; ++i)
-    *reinterpret_cast<u32x4*>(pa + G::TA + i * G::RSTEP * KB) = R.b[i];
+    *reinterpret_cast<u32x4*>(pa + G::TA + i * STEP) = R.b[i];
   if (P == NP - 1) {
 #pragma unroll
     for (int i = 0; i < G::SC; ++i) {
@@ -505,18 +504,18 @@ struct Scl {
 // Per-lane LDS read addresses, relative to a stage.
 struct RAddr {
   uint32_t fa, fb, sa, sb;
-  int g, half;
+  int half;
 };
 
+// Fragment of k-step s for lane (l32, half): chunk 2 s + half of row
+// row0 + 32 i + l32 = group row0/32 + i, slot l32.
 template <class G, int TM, int TN>
 __device__ __forceinline__ RAddr make_raddr(int wm, int wn, int lane) {
-  constexpr int KB = G::CPR * 16;
   RAddr r;
   const int l32 = lane & 31;
   r.half = lane >> 5;
-  r.g = swz<KB>(l32);
-  r.fa = (uint32_t)((wm * TM * 32 + l32) * KB);
-  r.fb = (uint32_t)(G::TA + (wn * TN * 32 + l32) * KB);
+  r.fa = (uint32_t)(wm * TM * G::GP + r.half * G::CP + l32 * 16);
+  r.fb = (uint32_t)(G::TA + wn * TN * G::GP + r.half * G::CP + l32 * 16);
   r.sa = (uint32_t)(G::SOFF + 4 * ((wm * 32 + l32) * 2 + r.half) * TM);
   r.sb = (uint32_t)(G::SBOFF + 4 * ((wn * 32 + l32) * 2 + r.half) * TN);
   return r;
@@ -524,16 +523,15 @@ __device__ __forceinline__ RAddr make_raddr(int wm, int wn, int lane) {
 
 template <class G, int TM, int TN, int S>
 __device__ __forceinline__ void read_frags(const uint8_t* st, const RAddr& ra, Frag<TM, TN>& F) {
-  constexpr int KB = G::CPR * 16;
-  const int co = ((2 * S + ra.half) ^ ra.g) << 4;
+  constexpr int co = 2 * S * G::CP;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const u32x4 q = *reinterpret_cast<const u32x4*>(st + ra.fa + co + i * 32 * KB);
+    const u32x4 q = *reinterpret_cast<const u32x4*>(st + ra.fa + co + i * G::GP);
     F.a[i] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
   }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    const u32x4 q = *reinterpret_cast<const u32x4*>(st + ra.fb + co + j * 32 * KB);
+    const u32x4 q = *reinterpret_cast<const u32x4*>(st + ra.fb + co + j * G::GP);
     F.b[j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
   }
 }
