@@ -15,8 +15,11 @@
 // E8M0 byte of that 32-block in the byte of its scale register picked by
 // op_sel. Output lane l, register r holds C[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32].
 //
-// Two kernel families. The large-tile kernel (namespace lt, below) serves
-// K % 256 == 0 with 32-bit operand offsets. The general kernel here serves
+// Three kernels. For K % 512 == 0 (every Llama-shaped product) the LDS-DMA
+// kernel (namespace dm, below) runs 256 x 256 tiles whose operands go
+// straight from global memory to LDS; for K % 256 == 0 the register-staged
+// large-tile kernel (namespace lt) runs the same tiles with 128-deep k-tiles;
+// both need 32-bit operand offsets. The general kernel here serves
 // any K % 32 == 0 and any M, N: a 256-thread work-group (4 waves, 2 x 2)
 // computes a 128 x 128 tile of C; each wave a 64 x 64 sub-tile (2 x 2 MFMA
 // tiles, 64 fp32 accumulators per lane). The k-loop steps 256 elements (128
@@ -321,28 +324,41 @@ __device__ __forceinline__ void make_offsets(Offs<G>& O, int64_t m0, int64_t n0,
   }
 }
 
+template <int SB> struct ScalePair;
+template <> struct ScalePair<8> { typedef u32x4 type; };
+template <> struct ScalePair<4> { typedef u32x2 type; };
+
+// Staging registers of one k-tile of A and B rows, and the scale bytes of
+// the scale row for two consecutive k-tiles (even tile in the low half).
 template <class G>
 struct Regs {
   u32x4 a[G::CA], b[G::CB];
-  u32x2 s[G::SC];  // SB bytes used (4 or 8)
+  typename ScalePair<G::SB>::type s[G::SC];
 };
 
 template <class G>
-__device__ __forceinline__ void gload(Regs<G>& R, const Offs<G>& O, const Src<G>& S, int kt) {
+__device__ __forceinline__ void gload_data(Regs<G>& R, const Offs<G>& O, const Src<G>& S, int kt) {
   constexpr int KB = G::CPR * 16;
-  const int ko = kt * KB, so = kt * G::SB;
+  const int ko = kt * KB;
 #pragma unroll
   for (int i = 0; i < G::CA; ++i) R.a[i] = __builtin_amdgcn_raw_buffer_load_b128(S.a, O.a[i], ko, 0);
 #pragma unroll
   for (int i = 0; i < G::CB; ++i) R.b[i] = __builtin_amdgcn_raw_buffer_load_b128(S.b, O.b[i], ko, 0);
+}
+
+// Scale bytes of the even k-tile kt and of kt + 1 in one load per scale row:
+// a scale row holds SB bytes per k-tile, so a load of 2 SB bytes per lane
+// touches half as many cache lines per byte as one k-tile's SB bytes would.
+template <class G>
+__device__ __forceinline__ void gload_scales(Regs<G>& R, const Offs<G>& O, const Src<G>& S,
+                                             int kt) {
+  const int so = kt * G::SB;
 #pragma unroll
   for (int i = 0; i < G::SC; ++i) {
-    if (G::SB == 8) {
+    if constexpr (G::SB == 8)
+      R.s[i] = __builtin_amdgcn_raw_buffer_load_b128(S.s[i], O.s[i], so, 0);
+    else
       R.s[i] = __builtin_amdgcn_raw_buffer_load_b64(S.s[i], O.s[i], so, 0);
-    } else {
-      const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(S.s[i], O.s[i], so, 0);
-      R.s[i] = u32x2{w, w};
-    }
   }
 }
 
@@ -395,8 +411,13 @@ struct Cfg {
   static constexpr int SB = KB / 16;                     // scale bytes per row per k-tile
   static constexpr int KSTEPS = KB / 32;                 // MFMA k-steps (64 elements each)
   // Fragment-major tiles: per group of 32 rows, chunk column c holds the 32
-  // rows' 16-byte chunk c back to back, padded to CP bytes.
-  static constexpr int CP = KB == 128 ? 544 : 576;       // chunk-column pitch
+  // rows' 16-byte chunk c back to back, padded to CP bytes. A 16-byte LDS
+  // write serves 8 lanes per cycle over 32 four-byte banks; the 8 lanes hold
+  // chunks c = 0..CPR-1 of 8 / CPR consecutive rows, at bank offsets
+  // (CP / 4) c + 4 r mod 32, which are all distinct for a pitch of 512 + 16
+  // bytes with 8 chunks per row and 512 + 32 with 4. Fragment reads take 16
+  // consecutive rows of one chunk column and do not depend on the pitch.
+  static constexpr int CP = KB == 128 ? 528 : 544;       // chunk-column pitch
   static constexpr int GP = (KB / 16) * CP;              // 32-row group pitch
   static constexpr int TA = (BM / 32) * GP, TB = (BN / 32) * GP;
   static constexpr int SOFF = TA + TB;                   // A scale words, then B scale words
@@ -443,10 +464,10 @@ __device__ __forceinline__ void make_spos(SPos<G, TM, TN>& P, int t) {
 }
 
 // Part P of NP of the staging registers -> LDS stage st (chunks in the
-// fragment-major layout; the scale words go with the last part). Thread t
-// holds chunk c = t % CPR of rows r0 + RSTEP i: group (r0 >> 5) + i RSTEP/32,
-// slot r0 & 31 of chunk column c.
-template <class G, int TM, int TN, int P, int NP>
+// fragment-major layout; the scale words, from half H of the scale pair, go
+// with the last part). Thread t holds chunk c = t % CPR of rows
+// r0 + RSTEP i: group (r0 >> 5) + i RSTEP/32, slot r0 & 31 of chunk column c.
+template <class G, int TM, int TN, int P, int NP, int H>
 __device__ __forceinline__ void lstore_part(const Regs<G>& R, const SPos<G, TM, TN>& SP,
                                             uint8_t* st, int t) {
   const int r0 = t / G::CPR, c = t % G::CPR;
@@ -461,7 +482,13 @@ __device__ __forceinline__ void lstore_part(const Regs<G>& R, const SPos<G, TM, 
   if (P == NP - 1) {
 #pragma unroll
     for (int i = 0; i < G::SC; ++i) {
-      const uint32_t lo = R.s[i].x, hi = R.s[i].y;
+      uint32_t lo, hi = 0;
+      if constexpr (G::SB == 8) {
+        lo = H ? R.s[i].z : R.s[i].x;
+        hi = H ? R.s[i].w : R.s[i].y;
+      } else {
+        lo = H ? R.s[i].y : R.s[i].x;
+      }
       uint32_t ev, od;
       if (G::SB == 8) {
         ev = (lo & 0xffu) | ((lo >> 8) & 0xff00u) | ((hi & 0xffu) << 16) | ((hi << 8) & 0xff000000u);
@@ -572,37 +599,42 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
-template <class G, int TM, int TN, int NS>
+template <class G, int TM, int TN, int NS, int C>
 struct Pipe {
   static constexpr int NM = TM * TN, NR = TM + TN;
   static constexpr int NWR = G::CA + G::CB + 2 * G::SC;   // LDS writes per k-tile
-  static constexpr int NLD = G::CA + G::CB + G::SC;       // global loads per k-tile
+  static constexpr int NLD = G::CA + G::CB + (C == 0 ? G::SC : 0);  // global loads
 };
 
-// One k-tile (stage C holds it; F0 / SCc hold its k-step-0 fragments and its
-// scales). Leaves the next k-tile's k-step-0 fragments in F0 and its scales in
-// SCn, the next k-tile written to stage C ^ 1, and tile k + 1 + NS loading
-// into the staging set just written.
+// One k-tile (stage C holds it, C = k % 2; F0 / SCc hold its k-step-0
+// fragments and its scales). Leaves the next k-tile's k-step-0 fragments in
+// F0 and its scales in SCn, the next k-tile written to stage C ^ 1, and tile
+// k + 2 loading into the staging set just written; an even k also loads the
+// scale pair of tiles k + 2 and k + 3 (the pair of k + 1 was used up here).
 template <class G, int TM, int TN, int NS, int C>
 __device__ __forceinline__ void ktile(uint8_t* lds, const RAddr& ra, Regs<G> (&R)[NS],
                                       const SPos<G, TM, TN>& SP, const Offs<G>& O,
                                       const Src<G>& S, Frag<TM, TN>& F0, Frag<TM, TN>& F1,
                                       const Scl<TM, TN>& SCc, Scl<TM, TN>& SCn,
                                       v16f (&acc)[TN][TM], int k, int nkt, int t) {
-  using PP = Pipe<G, TM, TN, NS>;
+  static_assert(NS == 1, "one staging set");
+  using PP = Pipe<G, TM, TN, NS, C>;
   uint8_t* cur = lds + C * G::STAGE;
   uint8_t* nxt = lds + (C ^ 1) * G::STAGE;
-  constexpr int X = (NS == 1) ? 0 : (C ^ 1);  // staging set holding tile k + 1
-  const int kl = min(k + 1 + NS, nkt - 1);
+  constexpr int X = 0;
+  // Prefetch indices clamp to the last k-tile (the last even one for the
+  // scale pair); the redundant loads land in a stage nobody reads again.
+  const int kl = min(k + 2, nkt - 1), kp = min(k + 2, nkt - 2);
   if constexpr (G::KSTEPS == 4) {
     read_frags<G, TM, TN, 1>(cur, ra, F1);
-    lstore_part<G, TM, TN, 0, 2>(R[X], SP, nxt, t);
+    lstore_part<G, TM, TN, 0, 2, C ^ 1>(R[X], SP, nxt, t);
     mfma_step<TM, TN, 0>(F0, SCc, acc);
     interleave<0, PP::NM, PP::NR, (G::CA + G::CB) / 2, 0>();
     __builtin_amdgcn_sched_barrier(0);
     read_frags<G, TM, TN, 2>(cur, ra, F0);
-    lstore_part<G, TM, TN, 1, 2>(R[X], SP, nxt, t);
-    gload<G>(R[X], O, S, kl);
+    lstore_part<G, TM, TN, 1, 2, C ^ 1>(R[X], SP, nxt, t);
+    gload_data<G>(R[X], O, S, kl);
+    if constexpr (C == 0) gload_scales<G>(R[X], O, S, kp);
     mfma_step<TM, TN, 1>(F1, SCc, acc);
     interleave<0, PP::NM, PP::NR, PP::NWR - (G::CA + G::CB) / 2, PP::NLD>();
     __builtin_amdgcn_sched_barrier(0);
@@ -618,8 +650,9 @@ __device__ __forceinline__ void ktile(uint8_t* lds, const RAddr& ra, Regs<G> (&R
     __builtin_amdgcn_sched_barrier(0);
   } else {
     read_frags<G, TM, TN, 1>(cur, ra, F1);
-    lstore_part<G, TM, TN, 0, 1>(R[X], SP, nxt, t);
-    gload<G>(R[X], O, S, kl);
+    lstore_part<G, TM, TN, 0, 1, C ^ 1>(R[X], SP, nxt, t);
+    gload_data<G>(R[X], O, S, kl);
+    if constexpr (C == 0) gload_scales<G>(R[X], O, S, kp);
     mfma_step<TM, TN, 0>(F0, SCc, acc);
     interleave<0, PP::NM, PP::NR, PP::NWR, PP::NLD>();
     __builtin_amdgcn_sched_barrier(0);
@@ -667,14 +700,13 @@ void gemm_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__
   make_spos<G, TM, TN>(SP, t);
   const RAddr ra = make_raddr<G, TM, TN>(wm, wn, lane);
 
-  // Prologue: k-tile 0 into stage 0; the staging sets then hold k-tiles
-  // 1 .. NS (prefetch indices clamp to the last k-tile; the redundant loads
-  // at the end land in a stage nobody reads again).
+  // Prologue: k-tile 0 into stage 0; the staging set then holds k-tile 1
+  // (nkt is even, so there is one) and the scale pair of tiles 0 and 1.
   Regs<G> R[NS];
-  gload<G>(R[0], O, S, 0);
-  if constexpr (NS == 2) gload<G>(R[1], O, S, min(1, nkt - 1));
-  lstore_part<G, TM, TN, 0, 1>(R[0], SP, lds, t);
-  gload<G>(R[0], O, S, min(NS == 1 ? 1 : 2, nkt - 1));
+  gload_data<G>(R[0], O, S, 0);
+  gload_scales<G>(R[0], O, S, 0);
+  lstore_part<G, TM, TN, 0, 1, 0>(R[0], SP, lds, t);
+  gload_data<G>(R[0], O, S, 1);
   lds_barrier();
   Frag<TM, TN> F0, F1;
   Scl<TM, TN> SCa, SCb;
@@ -765,6 +797,363 @@ hipError_t launch(const uint8_t* a, const uint8_t* as, const uint8_t* b, const u
 
 }  // namespace lt
 
+// Large-tile kernel fed by LDS DMA (K % 512 == 0). Same tile shape and MFMA
+// sequence as gemm_pipe_kernel (256 x 256 tiles, 8 waves of 128 x 64, 256-deep
+// k-tiles, identical operands per MFMA, so identical results); what differs is
+// how operands reach LDS and how C leaves:
+//  * buffer_load_dwordx4 ... lds: the 64 lanes of one instruction write 1 KiB
+//    of LDS at M0 + 16 lane, with no staging registers and no ds_write issued
+//    by the waves that run the MFMAs. A k-tile is 32 such blocks per operand
+//    (8 rows of 128 bytes each) and 16 dword blocks of scale bytes (32 rows of
+//    8 bytes each); each wave issues 10 of them;
+//  * tiles are row-major in LDS (128 bytes per row) with 16-byte chunk c of
+//    row r at slot c ^ ((r >> 1) & 7). The permutation is applied to which
+//    chunk a lane fetches, so a DMA block stays contiguous and 8 lanes fetch a
+//    whole 128-byte row; the 16 lanes of a fragment read (rows r .. r + 15 of
+//    one chunk) land on 16 distinct 4-bank groups;
+//  * scale rows stay as fetched (8 bytes per k-tile); a lane gathers the bytes
+//    of its 32-element half (even or odd blocks) with one v_perm per row;
+//  * the two stages are separate LDS arrays, so the compiler's wait tracking
+//    sees that a DMA into one stage does not feed reads of the other; a wave
+//    waits for its own DMAs (vmcnt) before the barrier that publishes them;
+//  * full fp32 tiles leave through LDS: a wave writes 64 x 64 of its block at
+//    a time (pitch 68 floats) and stores whole 256-byte row segments with
+//    non-temporal hints. Each store instruction then fills whole cache lines,
+//    and C streams past L2 instead of evicting the operand rows that the next
+//    tiles re-read.
+namespace dm {
+
+constexpr int BM = 256, BN = 256;
+constexpr int KB = 128;                      // bytes per operand row per k-tile
+constexpr int TILE = BM * KB;                // 32 KiB per operand
+constexpr int SOFF = 2 * TILE;               // scale rows: A (256 x 8 bytes), then B
+constexpr int STAGE = SOFF + (BM + BN) * 8;  // 69632 bytes
+
+// Wave layout: WM x WN waves of TM x TN MFMA tiles (TM * 32 x TN * 32 each).
+template <int WM_, int WN_, int TM_, int TN_>
+struct L {
+  static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_;
+  static constexpr int NW = WM * WN, NT = 64 * NW;
+  static constexpr int DA = 32 / NW;         // 1 KiB DMA blocks per operand per wave
+  static constexpr int DS = 8 / NW;          // 256-byte scale blocks per operand per wave
+  static constexpr int NDMA = 2 * DA + 2 * DS;  // DMA instructions per wave per k-tile
+  static constexpr int EP = TN * 32 + 4;     // epilogue staging pitch (floats)
+  static constexpr int ER = 64;              // rows per epilogue pass
+  static_assert(WM * TM * 32 == BM && WN * TN * 32 == BN, "256 x 256 tile");
+  static_assert(NW * DA == 32 && NW * DS == 8, "DMA blocks divide over the waves");
+  static_assert((NW / 2) * ER * EP * 4 <= STAGE, "half of the waves stage in one stage array");
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+using lt::rsrc_t;
+using lt::u32x2;
+using lt::u32x4;
+
+struct Rsrc {
+  rsrc_t a, b, sa, sb, none;  // none: zero records, every access out of range
+};
+
+// Per-lane buffer offsets of the thread's DMA rows (rows past M or N clamp to
+// the last row; their products are never stored).
+template <class G>
+struct Dma {
+  uint32_t a[G::DA], b[G::DA], sa[G::DS], sb[G::DS];
+};
+
+template <class G>
+__device__ __forceinline__ void make_dma(Dma<G>& D, int64_t m0, int64_t n0, int64_t M, int64_t N,
+                                         int64_t kbytes, int64_t kblk, int wave, int lane) {
+#pragma unroll
+  for (int u = 0; u < G::DA; ++u) {
+    const int row = 8 * (G::DA * wave + u) + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    D.a[u] = (uint32_t)(min(m0 + row, M - 1) * kbytes + c * 16);
+    D.b[u] = (uint32_t)(min(n0 + row, N - 1) * kbytes + c * 16);
+  }
+#pragma unroll
+  for (int v = 0; v < G::DS; ++v) {
+    const int srow = 32 * (G::DS * wave + v) + (lane >> 1), sw = (lane & 1) * 4;
+    D.sa[v] = (uint32_t)(min(m0 + srow, M - 1) * kblk + sw);
+    D.sb[v] = (uint32_t)(min(n0 + srow, N - 1) * kblk + sw);
+  }
+}
+
+// One LDS DMA instruction: lane l's 16 (or 4) bytes at buffer offset
+// voff + soff land at lds + 16 l (or 4 l).
+__device__ __forceinline__ void dma_b128(rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma_b32(rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, soff, 0, 0);
+}
+
+// k-tile kt of this wave's rows into stage st (when live is false every lane
+// is out of range: nothing is read and the stage is never read again).
+template <class G>
+__device__ __forceinline__ void dma_issue(uint8_t* st, const Rsrc& R, const Dma<G>& D, int kt,
+                                          bool live, int wave) {
+  const rsrc_t ra = live ? R.a : R.none, rb = live ? R.b : R.none;
+  const rsrc_t rsa = live ? R.sa : R.none, rsb = live ? R.sb : R.none;
+  const uint32_t ko = (uint32_t)kt * KB, so = (uint32_t)kt * 8;
+#pragma unroll
+  for (int u = 0; u < G::DA; ++u) dma_b128(ra, st + (G::DA * wave + u) * 1024, D.a[u], ko);
+#pragma unroll
+  for (int u = 0; u < G::DA; ++u) dma_b128(rb, st + TILE + (G::DA * wave + u) * 1024, D.b[u], ko);
+#pragma unroll
+  for (int v = 0; v < G::DS; ++v) dma_b32(rsa, st + SOFF + 256 * (G::DS * wave + v), D.sa[v], so);
+#pragma unroll
+  for (int v = 0; v < G::DS; ++v)
+    dma_b32(rsb, st + SOFF + 2048 + 256 * (G::DS * wave + v), D.sb[v], so);
+}
+
+// Per-lane LDS read offsets within a stage: fragment of k-step s (chunk
+// 2 s + half of row l32 of each 32-row group), and the lane's scale rows.
+struct RA {
+  uint32_t fa[4], fb[4], sa, sb, psel;
+};
+
+template <class G>
+__device__ __forceinline__ RA make_ra(int wm, int wn, int lane) {
+  RA r;
+  const int l32 = lane & 31, h = lane >> 5, key = (l32 >> 1) & 7;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint32_t off = (uint32_t)(l32 * KB + (((2 * s + h) ^ key) * 16));
+    r.fa[s] = (uint32_t)(wm * G::TM * 32 * KB) + off;
+    r.fb[s] = (uint32_t)(TILE + wn * G::TN * 32 * KB) + off;
+  }
+  r.sa = (uint32_t)(SOFF + (wm * G::TM * 32 + l32) * 8);
+  r.sb = (uint32_t)(SOFF + 2048 + (wn * G::TN * 32 + l32) * 8);
+  r.psel = h ? 0x07050301u : 0x06040200u;  // bytes 1,3,5,7 or 0,2,4,6 of the row's 8
+  return r;
+}
+
+template <class G, int S>
+__device__ __forceinline__ void read_frags(const uint8_t* st, const RA& ra,
+                                           lt::Frag<G::TM, G::TN>& F) {
+#pragma unroll
+  for (int i = 0; i < G::TM; ++i) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(st + ra.fa[S] + i * 32 * KB);
+    F.a[i] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int j = 0; j < G::TN; ++j) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(st + ra.fb[S] + j * 32 * KB);
+    F.b[j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+  }
+}
+
+template <class G>
+__device__ __forceinline__ void read_scales(const uint8_t* st, const RA& ra,
+                                            lt::Scl<G::TM, G::TN>& S) {
+#pragma unroll
+  for (int i = 0; i < G::TM; ++i) {
+    const u32x2 q = *reinterpret_cast<const u32x2*>(st + ra.sa + i * 256);
+    S.a[i] = (int)__builtin_amdgcn_perm(q.y, q.x, ra.psel);
+  }
+#pragma unroll
+  for (int j = 0; j < G::TN; ++j) {
+    const u32x2 q = *reinterpret_cast<const u32x2*>(st + ra.sb + j * 256);
+    S.b[j] = (int)__builtin_amdgcn_perm(q.y, q.x, ra.psel);
+  }
+}
+
+// s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One k-tile k in stage C (F0 / SCc hold its k-step-0 fragments and its
+// scales). The barrier before the last k-step publishes tile k + 1 (every
+// wave waited for its own DMAs of it) and retires stage C, which then
+// receives tile k + 2 while the last MFMAs of tile k run.
+template <class G, int C>
+__device__ __forceinline__ void ktile(uint8_t* st0, uint8_t* st1, const RA& ra, const Rsrc& R,
+                                      const Dma<G>& D, lt::Frag<G::TM, G::TN>& F0,
+                                      lt::Frag<G::TM, G::TN>& F1, const lt::Scl<G::TM, G::TN>& SCc,
+                                      lt::Scl<G::TM, G::TN>& SCn, v16f (&acc)[G::TN][G::TM], int k,
+                                      int nkt, int wave) {
+  constexpr int TM = G::TM, TN = G::TN, NM = TM * TN, NR = TM + TN;
+  uint8_t* cur = C ? st1 : st0;
+  uint8_t* nxt = C ? st0 : st1;
+  read_frags<G, 1>(cur, ra, F1);
+  lt::mfma_step<TM, TN, 0>(F0, SCc, acc);
+  lt::interleave<0, NM, NR, 0, 0>();
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags<G, 2>(cur, ra, F0);
+  lt::mfma_step<TM, TN, 1>(F1, SCc, acc);
+  lt::interleave<0, NM, NR, 0, 0>();
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags<G, 3>(cur, ra, F1);
+  lt::mfma_step<TM, TN, 2>(F0, SCc, acc);
+  lt::interleave<0, NM, NR, 0, 0>();
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm<0>();
+  lt::lds_barrier();
+  read_scales<G>(nxt, ra, SCn);
+  read_frags<G, 0>(nxt, ra, F0);
+  dma_issue<G>(cur, R, D, min(k + 2, nkt - 1), k + 2 < nkt, wave);
+  lt::mfma_step<TM, TN, 3>(F1, SCc, acc);
+  lt::interleave<0, NM, 2 * NR, 0, G::NDMA>();
+  // the scale byte gathers (v_perm) wait for their reads: keep them last
+  __builtin_amdgcn_sched_group_barrier(0x002, NR, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <class G, int OUT, bool VEC>
+__global__ __attribute__((amdgpu_flat_work_group_size(G::NT, G::NT),
+                          amdgpu_waves_per_eu(8 / G::NW)))
+void gemm_dma_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
+                     const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, int64_t M,
+                     int64_t N, int64_t K, void* __restrict__ C) {
+  constexpr int TM = G::TM, TN = G::TN;
+  __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave / G::WN, wn = wave % G::WN;
+  const int64_t ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
+  int64_t tm, tn;
+  lt::tile_of<lt::GROUP_M>(blockIdx.x, gridDim.x, ntm, ntn, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const int64_t kbytes = K / 2, kblk = K / 32;
+  const int nkt = (int)(kbytes / KB);
+  const int arow0 = wm * TM * 32, brow0 = wn * TN * 32;
+
+  v16f acc[TN][TM];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
+
+  Rsrc R;
+  R.a = lt::make_rsrc(A, M * kbytes);
+  R.b = lt::make_rsrc(B, N * kbytes);
+  R.sa = lt::make_rsrc(As, M * kblk);
+  R.sb = lt::make_rsrc(Bs, N * kblk);
+  R.none = lt::make_rsrc(A, 0);
+  Dma<G> D;
+  make_dma<G>(D, m0, n0, M, N, kbytes, kblk, wave, lane);
+  const RA ra = make_ra<G>(wm, wn, lane);
+
+  // Prologue: k-tiles 0 and 1 (nkt is even, so both exist) into the stages.
+  dma_issue<G>(st0, R, D, 0, true, wave);
+  dma_issue<G>(st1, R, D, 1, true, wave);
+  wait_vm<G::NDMA>();  // loads complete in issue order: tile 0's have landed
+  lt::lds_barrier();
+  lt::Frag<TM, TN> F0, F1;
+  lt::Scl<TM, TN> SCa, SCb;
+  read_scales<G>(st0, ra, SCa);
+  read_frags<G, 0>(st0, ra, F0);
+
+  for (int k = 0; k < nkt; k += 2) {
+    ktile<G, 0>(st0, st1, ra, R, D, F0, F1, SCa, SCb, acc, k, nkt, wave);
+    ktile<G, 1>(st0, st1, ra, R, D, F0, F1, SCb, SCa, acc, k + 1, nkt, wave);
+  }
+
+  // Epilogue: acc[j][i] register 4q + e holds C[m][n] with
+  // m = m0 + arow0 + 32 i + (lane & 31), n = n0 + brow0 + 32 j + 8 q + 4 (lane >> 5) + e.
+  const int half = lane >> 5, l32 = lane & 31;
+  const bool full = VEC && (m0 + BM <= M) && (n0 + BN <= N);
+  if (OUT == 0 && full) {
+    // The last (out-of-range) DMAs wrote into the stages: let them land and
+    // every wave finish its reads before the stages are reused.
+    wait_vm<0>();
+    lt::lds_barrier();
+    constexpr int HW = G::NW / 2, EP = G::EP, ER = G::ER;
+    float* wl = reinterpret_cast<float*>(wave < HW ? st0 : st1) + (wave % HW) * ER * EP;
+    constexpr int LPR = TN * 32 / 4, RPI = 64 / LPR;  // lanes per row segment, rows per store
+    const int rr = lane / LPR, cc = 4 * (lane % LPR);
+#pragma unroll
+    for (int p = 0; p < TM * 32 / ER; ++p) {
+#pragma unroll
+      for (int ii = 0; ii < ER / 32; ++ii) {
+        const int i = p * (ER / 32) + ii;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<f32x4*>(wl + (ii * 32 + l32) * EP + j * 32 + 8 * q + 4 * half) =
+                f32x4{acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
+                      acc[j][i][4 * q + 3]};
+      }
+#pragma unroll
+      for (int s = 0; s < ER / RPI; ++s) {
+        const int row = s * RPI + rr;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(wl + row * EP + cc);
+        const int64_t m = m0 + arow0 + p * ER + row;
+        __builtin_nontemporal_store(
+            v, reinterpret_cast<f32x4*>(static_cast<float*>(C) + m * N + n0 + brow0 + cc));
+      }
+    }
+    return;
+  }
+  if (full) {  // bf16 out: straight from the accumulators
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t m = m0 + arow0 + i * 32 + l32;
+      uint16_t* p = static_cast<uint16_t*>(C) + m * N + n0 + brow0 + 4 * half;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = bf16_rne(acc[j][i][4 * q]) | (bf16_rne(acc[j][i][4 * q + 1]) << 16);
+          const uint32_t hi = bf16_rne(acc[j][i][4 * q + 2]) | (bf16_rne(acc[j][i][4 * q + 3]) << 16);
+          *reinterpret_cast<uint2*>(p + j * 32 + 8 * q) = make_uint2(lo, hi);
+        }
+    }
+    return;
+  }
+  // Edge tiles (or unaligned C): element-wise, predicated.
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t m = m0 + arow0 + i * 32 + l32;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t n = n0 + brow0 + j * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (m < M && n < N) {
+          if (OUT == 0)
+            static_cast<float*>(C)[m * N + n] = acc[j][i][r];
+          else
+            static_cast<uint16_t*>(C)[m * N + n] = (uint16_t)bf16_rne(acc[j][i][r]);
+        }
+      }
+  }
+}
+
+template <class G>
+hipError_t launch(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
+                  int64_t M, int64_t N, int64_t K, void* C, int out_dtype, hipStream_t stream) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const bool vec = (N % 4 == 0) && ((uintptr_t)C % 16 == 0);
+  const dim3 grid((unsigned)tiles), blk(G::NT);
+  if (out_dtype == 0) {
+    if (vec)
+      hipLaunchKernelGGL((gemm_dma_kernel<G, 0, true>), grid, blk, 0, stream, a, as, b, bs, M, N,
+                         K, C);
+    else
+      hipLaunchKernelGGL((gemm_dma_kernel<G, 0, false>), grid, blk, 0, stream, a, as, b, bs, M,
+                         N, K, C);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((gemm_dma_kernel<G, 1, true>), grid, blk, 0, stream, a, as, b, bs, M, N,
+                         K, C);
+    else
+      hipLaunchKernelGGL((gemm_dma_kernel<G, 1, false>), grid, blk, 0, stream, a, as, b, bs, M,
+                         N, K, C);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dm
+
 }  // namespace
 
 hipError_t launch_gemm(const void* Aq, const void* As, const void* Bq, const void* Bs, int64_t M,
@@ -777,10 +1166,14 @@ hipError_t launch_gemm(const void* Aq, const void* As, const void* Bq, const voi
   // Large-tile paths (the main loop runs k-tiles in pairs, so K must hold
   // an even number of them; 32-bit per-lane operand offsets): 256 x 256
   // tiles, 8 waves of 128 x 64, with 256-deep k-tiles when K % 512 == 0 and
-  // 128-deep ones when only K % 256 == 0.
+  // the scale arrays are 16-byte aligned (scale pairs are 16-byte loads), and
+  // 128-deep ones when only K % 256 == 0 (8-byte pairs).
   const bool off32 = (M * (K / 2) < (int64_t(1) << 32)) && (N * (K / 2) < (int64_t(1) << 32));
   const bool sc_al = ((uintptr_t)As % 8 == 0) && ((uintptr_t)Bs % 8 == 0);
+  const bool sc_al16 = ((uintptr_t)As % 16 == 0) && ((uintptr_t)Bs % 16 == 0);
   if (off32 && sc_al && K % 512 == 0)
+    return dm::launch<dm::L<2, 4, 4, 2>>(a, as, b, bs, M, N, K, C, out_dtype, stream);
+  if (off32 && sc_al16 && K % 512 == 0)
     return lt::launch<2, 4, 4, 2, 128, 1, 2>(a, as, b, bs, M, N, K, C, out_dtype, stream);
   if (off32 && sc_al && K % 256 == 0)
     return lt::launch<2, 4, 4, 2, 64, 1, 2>(a, as, b, bs, M, N, K, C, out_dtype, stream);

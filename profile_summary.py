@@ -25,8 +25,20 @@ from collections import defaultdict
 
 
 def short(name: str) -> str:
-    m = re.search(r"::(\w+_kernel(?:<[^>]*>)?)\(", name)
-    return m.group(1) if m else name[:60]
+    """Kernel name with its template arguments, without namespaces and parameters."""
+    m = re.search(r"(\w+_kernel)\b", name)
+    if not m:
+        return name[:60]
+    out, i = m.group(1), m.end()
+    if i < len(name) and name[i] == "<":
+        depth, j = 0, i
+        while j < len(name):
+            depth += {"<": 1, ">": -1}.get(name[j], 0)
+            j += 1
+            if depth == 0:
+                break
+        out += re.sub(r"(\w+::|\(anonymous namespace\)::)", "", name[i:j])
+    return out
 
 
 def trace_summary(path):
