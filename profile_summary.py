@@ -14,7 +14,8 @@ usage: python profile_summary.py TRACE_CSV [--pmc COUNTER_CSV]
 WRITE_SIZE, in KiB per dispatch) into HBM bytes per GEMM launch. Each counter
 is scaled by bytes / counter of the 1 GiB copy kernel in the same run (the
 copy reads and writes exactly 2^30 bytes), and the result is written with
-the sha256 of the kernel source it was measured on.
+the sha256 of the kernel source's code (comments and blank lines dropped)
+it was measured on.
 """
 from __future__ import annotations
 
@@ -79,8 +80,17 @@ def _per_kernel(path, counter):
     return out
 
 
-def traffic(fetch_csv, write_csv, kernel_src, out_json):
+def sha_of(path):
+    """sha256 (first 16 hex) of a source file's code: // comments and blank
+    lines are dropped, so a comment edit does not mark counters as stale."""
     import hashlib
+    with open(path) as f:
+        lines = [re.sub(r"//.*", "", ln).rstrip() for ln in f]
+    code = "\n".join(ln for ln in lines if ln.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
+
+
+def traffic(fetch_csv, write_csv, kernel_src, out_json):
     import json
     fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
     write = _per_kernel(write_csv, "WRITE_SIZE")
@@ -93,8 +103,7 @@ def traffic(fetch_csv, write_csv, kernel_src, out_json):
     w_factor = copy_bytes / (sum(write[ck]) / len(write[ck]) * 1024.0)
     g_fetch = sum(fetch[gk]) / len(fetch[gk]) * 1024.0 * f_factor
     g_write = sum(write[gk]) / len(write[gk]) * 1024.0 * w_factor
-    with open(kernel_src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    sha = sha_of(kernel_src)
     rec = {"kernel": gk, "kernel_sha": sha, "bytes_per_launch": round(g_fetch + g_write),
            "read_bytes": round(g_fetch), "write_bytes": round(g_write),
            "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
