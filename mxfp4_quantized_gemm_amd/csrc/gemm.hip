@@ -1044,8 +1044,13 @@ void gemm_dma_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   // Prologue: k-tiles 0 and 1 (nkt is even, so both exist) into the stages.
   dma_issue<G>(st0, R, D, 0, true, wave);
   dma_issue<G>(st1, R, D, 1, true, wave);
-  wait_vm<G::NDMA>();  // loads complete in issue order: tile 0's have landed
-  lt::lds_barrier();
+  // Loads complete in issue order, so this wave's DMAs of tile 0 have landed
+  // once at most NDMA are outstanding. No LDS reads precede this barrier, so
+  // it needs no release fence (which would also wait for tile 1's DMAs); the
+  // acquire fence keeps the reads of stage 0 below it.
+  wait_vm<G::NDMA>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   lt::Frag<TM, TN> F0, F1;
   lt::Scl<TM, TN> SCa, SCb;
   read_scales<G>(st0, ra, SCa);
