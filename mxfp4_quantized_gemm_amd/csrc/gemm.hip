@@ -15,11 +15,11 @@
 // E8M0 byte of that 32-block in the byte of its scale register picked by
 // op_sel. Output lane l, register r holds C[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32].
 //
-// Three kernels. For K % 512 == 0 (every Llama-shaped product) the LDS-DMA
+// Three kernels. For K % 2048 == 0 (every Llama-shaped product) the LDS-DMA
 // kernel (namespace dm, below) runs 256 x 256 tiles whose operands go
 // straight from global memory to LDS; for K % 256 == 0 the register-staged
-// large-tile kernel (namespace lt) runs the same tiles with 128-deep k-tiles;
-// both need 32-bit operand offsets. The general kernel here serves
+// large-tile kernel (namespace lt) runs the same tiles with 256- or 128-deep
+// k-tiles; both need 32-bit operand offsets. The general kernel here serves
 // any K % 32 == 0 and any M, N: a 256-thread work-group (4 waves, 2 x 2)
 // computes a 128 x 128 tile of C; each wave a 64 x 64 sub-tile (2 x 2 MFMA
 // tiles, 64 fp32 accumulators per lane). The k-loop steps 256 elements (128
@@ -797,26 +797,32 @@ hipError_t launch(const uint8_t* a, const uint8_t* as, const uint8_t* b, const u
 
 }  // namespace lt
 
-// Large-tile kernel fed by LDS DMA (K % 512 == 0). Same tile shape and MFMA
+// Large-tile kernel fed by LDS DMA (K % 2048 == 0). Same tile shape and MFMA
 // sequence as gemm_pipe_kernel (256 x 256 tiles, 8 waves of 128 x 64, 256-deep
 // k-tiles, identical operands per MFMA, so identical results); what differs is
 // how operands reach LDS and how C leaves:
 //  * buffer_load_dwordx4 ... lds: the 64 lanes of one instruction write 1 KiB
 //    of LDS at M0 + 16 lane, with no staging registers and no ds_write issued
 //    by the waves that run the MFMAs. A k-tile is 32 such blocks per operand
-//    (8 rows of 128 bytes each) and 16 dword blocks of scale bytes (32 rows of
-//    8 bytes each); each wave issues 10 of them;
+//    (8 rows of 128 bytes each), 4 per wave;
 //  * tiles are row-major in LDS (128 bytes per row) with 16-byte chunk c of
 //    row r at slot c ^ ((r >> 1) & 7). The permutation is applied to which
 //    chunk a lane fetches, so a DMA block stays contiguous and 8 lanes fetch a
 //    whole 128-byte row; the 16 lanes of a fragment read (rows r .. r + 15 of
 //    one chunk) land on 16 distinct 4-bank groups;
-//  * scale rows stay as fetched (8 bytes per k-tile); a lane gathers the bytes
-//    of its 32-element half (even or odd blocks) with one v_perm per row;
-//  * the two stages are separate LDS arrays, so the compiler's wait tracking
-//    sees that a DMA into one stage does not feed reads of the other; a wave
-//    waits for its own DMAs (vmcnt) before the barrier that publishes them;
-//  * full fp32 tiles leave through LDS: a wave writes 64 x 64 of its block at
+//  * scale bytes arrive in groups of 4 k-tiles (32 bytes of every scale row,
+//    two lanes per row), double-buffered. The load unit's cost grows with the
+//    number of cache lines an instruction touches, not with its bytes, and a
+//    scale row holds only 8 bytes per k-tile: fetched per k-tile, the scales
+//    touched as many lines as the operand rows themselves (measured: the
+//    operand stream of the gate+up product took 273 us with per-k-tile scale
+//    rows against 163 us without them). A lane gathers the bytes of its
+//    32-element half (even or odd blocks) with one v_perm per row;
+//  * the stages and the scale buffers are separate LDS arrays, so the
+//    compiler's wait tracking sees that a DMA into one does not feed reads of
+//    another; a wave waits for its own DMAs (vmcnt) before the barrier that
+//    publishes them;
+//  * full fp32 tiles leave through LDS: a wave writes 32 x 64 of its block at
 //    a time (pitch 68 floats) and stores whole 256-byte row segments with
 //    non-temporal hints. Each store instruction then fills whole cache lines,
 //    and C streams past L2 instead of evicting the operand rows that the next
@@ -826,8 +832,8 @@ namespace dm {
 constexpr int BM = 256, BN = 256;
 constexpr int KB = 128;                      // bytes per operand row per k-tile
 constexpr int TILE = BM * KB;                // 32 KiB per operand
-constexpr int SOFF = 2 * TILE;               // scale rows: A (256 x 8 bytes), then B
-constexpr int STAGE = SOFF + (BM + BN) * 8;  // 69632 bytes
+constexpr int STAGE = 2 * TILE;             // A rows then B rows of one k-tile
+constexpr int SGB = (BM + BN) * 32;         // scale group: 4 k-tiles x 8 bytes per row
 
 // Wave layout: WM x WN waves of TM x TN MFMA tiles (TM * 32 x TN * 32 each).
 template <int WM_, int WN_, int TM_, int TN_>
@@ -835,10 +841,10 @@ struct L {
   static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_;
   static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int DA = 32 / NW;         // 1 KiB DMA blocks per operand per wave
-  static constexpr int DS = 8 / NW;          // 256-byte scale blocks per operand per wave
-  static constexpr int NDMA = 2 * DA + 2 * DS;  // DMA instructions per wave per k-tile
+  static constexpr int DS = 8 / NW;          // 1 KiB scale-group blocks per operand per wave
+  static constexpr int NDMA = 2 * DA;        // data DMA instructions per wave per k-tile
   static constexpr int EP = TN * 32 + 4;     // epilogue staging pitch (floats)
-  static constexpr int ER = 64;              // rows per epilogue pass
+  static constexpr int ER = 32;              // rows per epilogue pass
   static_assert(WM * TM * 32 == BM && WN * TN * 32 == BN, "256 x 256 tile");
   static_assert(NW * DA == 32 && NW * DS == 8, "DMA blocks divide over the waves");
   static_assert((NW / 2) * ER * EP * 4 <= STAGE, "half of the waves stage in one stage array");
@@ -873,9 +879,10 @@ __device__ __forceinline__ void make_dma(Dma<G>& D, int64_t m0, int64_t n0, int6
   }
 #pragma unroll
   for (int v = 0; v < G::DS; ++v) {
-    const int srow = 32 * (G::DS * wave + v) + (lane >> 1), sw = (lane & 1) * 4;
-    D.sa[v] = (uint32_t)(min(m0 + srow, M - 1) * kblk + sw);
-    D.sb[v] = (uint32_t)(min(n0 + srow, N - 1) * kblk + sw);
+    const int srow = 32 * (G::DS * wave + v) + 16 * (lane >> 5) + (lane & 15);
+    const int sh = (lane >> 4) & 1;
+    D.sa[v] = (uint32_t)(min(m0 + srow, M - 1) * kblk + 16 * sh);
+    D.sb[v] = (uint32_t)(min(n0 + srow, N - 1) * kblk + 16 * sh);
   }
 }
 
@@ -894,17 +901,24 @@ template <class G>
 __device__ __forceinline__ void dma_issue(uint8_t* st, const Rsrc& R, const Dma<G>& D, int kt,
                                           bool live, int wave) {
   const rsrc_t ra = live ? R.a : R.none, rb = live ? R.b : R.none;
-  const rsrc_t rsa = live ? R.sa : R.none, rsb = live ? R.sb : R.none;
-  const uint32_t ko = (uint32_t)kt * KB, so = (uint32_t)kt * 8;
+  const uint32_t ko = (uint32_t)kt * KB;
 #pragma unroll
   for (int u = 0; u < G::DA; ++u) dma_b128(ra, st + (G::DA * wave + u) * 1024, D.a[u], ko);
 #pragma unroll
   for (int u = 0; u < G::DA; ++u) dma_b128(rb, st + TILE + (G::DA * wave + u) * 1024, D.b[u], ko);
+}
+
+// Scale group g (4 k-tiles, 32 bytes of every scale row) into sg: 1 KiB
+// blocks of 32 rows, unit u = 32 (r / 16) + 16 s + r % 16 holds half s of row r.
+template <class G>
+__device__ __forceinline__ void dma_scales(uint8_t* sg, const Rsrc& R, const Dma<G>& D, int g,
+                                           bool live, int wave) {
+  const rsrc_t rsa = live ? R.sa : R.none, rsb = live ? R.sb : R.none;
+  const uint32_t so = (uint32_t)g * 32;
 #pragma unroll
-  for (int v = 0; v < G::DS; ++v) dma_b32(rsa, st + SOFF + 256 * (G::DS * wave + v), D.sa[v], so);
+  for (int v = 0; v < G::DS; ++v) dma_b128(rsa, sg + 1024 * (G::DS * wave + v), D.sa[v], so);
 #pragma unroll
-  for (int v = 0; v < G::DS; ++v)
-    dma_b32(rsb, st + SOFF + 2048 + 256 * (G::DS * wave + v), D.sb[v], so);
+  for (int v = 0; v < G::DS; ++v) dma_b128(rsb, sg + 8192 + 1024 * (G::DS * wave + v), D.sb[v], so);
 }
 
 // Per-lane LDS read offsets within a stage: fragment of k-step s (chunk
@@ -923,8 +937,9 @@ __device__ __forceinline__ RA make_ra(int wm, int wn, int lane) {
     r.fa[s] = (uint32_t)(wm * G::TM * 32 * KB) + off;
     r.fb[s] = (uint32_t)(TILE + wn * G::TN * 32 * KB) + off;
   }
-  r.sa = (uint32_t)(SOFF + (wm * G::TM * 32 + l32) * 8);
-  r.sb = (uint32_t)(SOFF + 2048 + (wn * G::TN * 32 + l32) * 8);
+  const uint32_t u = (uint32_t)(16 * (32 * (l32 >> 4) + (l32 & 15)));
+  r.sa = (uint32_t)(wm * G::TM * 1024) + u;
+  r.sb = (uint32_t)(8192 + wn * G::TN * 1024) + u;
   r.psel = h ? 0x07050301u : 0x06040200u;  // bytes 1,3,5,7 or 0,2,4,6 of the row's 8
   return r;
 }
@@ -944,18 +959,21 @@ __device__ __forceinline__ void read_frags(const uint8_t* st, const RA& ra,
   }
 }
 
-template <class G>
-__device__ __forceinline__ void read_scales(const uint8_t* st, const RA& ra,
+template <class G, int P>
+__device__ __forceinline__ void read_scales(const uint8_t* sg, const RA& ra,
                                             lt::Scl<G::TM, G::TN>& S) {
+  constexpr int so = 256 * (P >> 1);
 #pragma unroll
   for (int i = 0; i < G::TM; ++i) {
-    const u32x2 q = *reinterpret_cast<const u32x2*>(st + ra.sa + i * 256);
-    S.a[i] = (int)__builtin_amdgcn_perm(q.y, q.x, ra.psel);
+    const u32x4 q = *reinterpret_cast<const u32x4*>(sg + ra.sa + so + i * 1024);
+    S.a[i] = (P & 1) ? (int)__builtin_amdgcn_perm(q.w, q.z, ra.psel)
+                     : (int)__builtin_amdgcn_perm(q.y, q.x, ra.psel);
   }
 #pragma unroll
   for (int j = 0; j < G::TN; ++j) {
-    const u32x2 q = *reinterpret_cast<const u32x2*>(st + ra.sb + j * 256);
-    S.b[j] = (int)__builtin_amdgcn_perm(q.y, q.x, ra.psel);
+    const u32x4 q = *reinterpret_cast<const u32x4*>(sg + ra.sb + so + j * 1024);
+    S.b[j] = (P & 1) ? (int)__builtin_amdgcn_perm(q.w, q.z, ra.psel)
+                     : (int)__builtin_amdgcn_perm(q.y, q.x, ra.psel);
   }
 }
 
@@ -971,14 +989,18 @@ __device__ __forceinline__ void wait_vm() {
 // wave waited for its own DMAs of it) and retires stage C, which then
 // receives tile k + 2 while the last MFMAs of tile k run.
 template <class G, int C>
-__device__ __forceinline__ void ktile(uint8_t* st0, uint8_t* st1, const RA& ra, const Rsrc& R,
+__device__ __forceinline__ void ktile(uint8_t* st0, uint8_t* st1, uint8_t* sg0, uint8_t* sg1,
+                                      const RA& ra, const Rsrc& R,
                                       const Dma<G>& D, lt::Frag<G::TM, G::TN>& F0,
                                       lt::Frag<G::TM, G::TN>& F1, const lt::Scl<G::TM, G::TN>& SCc,
                                       lt::Scl<G::TM, G::TN>& SCn, v16f (&acc)[G::TN][G::TM], int k,
                                       int nkt, int wave) {
   constexpr int TM = G::TM, TN = G::TN, NM = TM * TN, NR = TM + TN;
-  uint8_t* cur = C ? st1 : st0;
-  uint8_t* nxt = C ? st0 : st1;
+  uint8_t* cur = (C & 1) ? st1 : st0;
+  uint8_t* nxt = (C & 1) ? st0 : st1;
+  uint8_t* sgn = (((C + 1) >> 2) & 1) ? sg1 : sg0;   // scale group of tile k + 1
+  uint8_t* sgw = (((C + 5) >> 2) & 1) ? sg1 : sg0;   // group (k + 5) / 4, written when C % 4 == 3
+  constexpr bool SG = (C & 3) == 3;
   read_frags<G, 1>(cur, ra, F1);
   lt::mfma_step<TM, TN, 0>(F0, SCc, acc);
   lt::interleave<0, NM, NR, 0, 0>();
@@ -993,11 +1015,15 @@ __device__ __forceinline__ void ktile(uint8_t* st0, uint8_t* st1, const RA& ra, 
   __builtin_amdgcn_sched_barrier(0);
   wait_vm<0>();
   lt::lds_barrier();
-  read_scales<G>(nxt, ra, SCn);
+  read_scales<G, (C + 1) & 3>(sgn, ra, SCn);
   read_frags<G, 0>(nxt, ra, F0);
   dma_issue<G>(cur, R, D, min(k + 2, nkt - 1), k + 2 < nkt, wave);
+  if constexpr (SG) {
+    const int g = (k + 5) >> 2, ng = nkt >> 2;
+    dma_scales<G>(sgw, R, D, min(g, ng - 1), g < ng, wave);
+  }
   lt::mfma_step<TM, TN, 3>(F1, SCc, acc);
-  lt::interleave<0, NM, 2 * NR, 0, G::NDMA>();
+  lt::interleave<0, NM, 2 * NR, 0, G::NDMA + (SG ? 2 * G::DS : 0)>();
   // the scale byte gathers (v_perm) wait for their reads: keep them last
   __builtin_amdgcn_sched_group_barrier(0x002, NR, 0);
   __builtin_amdgcn_sched_barrier(0);
@@ -1005,13 +1031,15 @@ __device__ __forceinline__ void ktile(uint8_t* st0, uint8_t* st1, const RA& ra, 
 
 template <class G, int OUT, bool VEC>
 __global__ __attribute__((amdgpu_flat_work_group_size(G::NT, G::NT),
-                          amdgpu_waves_per_eu(8 / G::NW)))
+                          amdgpu_waves_per_eu(G::NW == 8 ? 2 : 1)))
 void gemm_dma_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
                      const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, int64_t M,
                      int64_t N, int64_t K, void* __restrict__ C) {
   constexpr int TM = G::TM, TN = G::TN;
   __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sg0[SGB];
+  __shared__ __attribute__((aligned(16))) uint8_t sg1[SGB];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave / G::WN, wn = wave % G::WN;
@@ -1041,28 +1069,30 @@ void gemm_dma_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   make_dma<G>(D, m0, n0, M, N, kbytes, kblk, wave, lane);
   const RA ra = make_ra<G>(wm, wn, lane);
 
-  // Prologue: k-tiles 0 and 1 (nkt is even, so both exist) into the stages.
+  // Prologue: scale group 0, k-tiles 0 and 1, scale group 1 (nkt % 8 == 0).
+  dma_scales<G>(sg0, R, D, 0, true, wave);
   dma_issue<G>(st0, R, D, 0, true, wave);
   dma_issue<G>(st1, R, D, 1, true, wave);
-  // Loads complete in issue order, so this wave's DMAs of tile 0 have landed
-  // once at most NDMA are outstanding. No LDS reads precede this barrier, so
-  // it needs no release fence (which would also wait for tile 1's DMAs); the
-  // acquire fence keeps the reads of stage 0 below it.
-  wait_vm<G::NDMA>();
+  dma_scales<G>(sg1, R, D, 1, true, wave);
+  wait_vm<G::NDMA + 2 * G::DS>();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   lt::Frag<TM, TN> F0, F1;
   lt::Scl<TM, TN> SCa, SCb;
-  read_scales<G>(st0, ra, SCa);
+  read_scales<G, 0>(sg0, ra, SCa);
   read_frags<G, 0>(st0, ra, F0);
 
-  for (int k = 0; k < nkt; k += 2) {
-    ktile<G, 0>(st0, st1, ra, R, D, F0, F1, SCa, SCb, acc, k, nkt, wave);
-    ktile<G, 1>(st0, st1, ra, R, D, F0, F1, SCb, SCa, acc, k + 1, nkt, wave);
+  for (int k = 0; k < nkt; k += 8) {
+    ktile<G, 0>(st0, st1, sg0, sg1, ra, R, D, F0, F1, SCa, SCb, acc, k, nkt, wave);
+    ktile<G, 1>(st0, st1, sg0, sg1, ra, R, D, F0, F1, SCb, SCa, acc, k + 1, nkt, wave);
+    ktile<G, 2>(st0, st1, sg0, sg1, ra, R, D, F0, F1, SCa, SCb, acc, k + 2, nkt, wave);
+    ktile<G, 3>(st0, st1, sg0, sg1, ra, R, D, F0, F1, SCb, SCa, acc, k + 3, nkt, wave);
+    ktile<G, 4>(st0, st1, sg0, sg1, ra, R, D, F0, F1, SCa, SCb, acc, k + 4, nkt, wave);
+    ktile<G, 5>(st0, st1, sg0, sg1, ra, R, D, F0, F1, SCb, SCa, acc, k + 5, nkt, wave);
+    ktile<G, 6>(st0, st1, sg0, sg1, ra, R, D, F0, F1, SCa, SCb, acc, k + 6, nkt, wave);
+    ktile<G, 7>(st0, st1, sg0, sg1, ra, R, D, F0, F1, SCb, SCa, acc, k + 7, nkt, wave);
   }
 
-  // Epilogue: acc[j][i] register 4q + e holds C[m][n] with
-  // m = m0 + arow0 + 32 i + (lane & 31), n = n0 + brow0 + 32 j + 8 q + 4 (lane >> 5) + e.
   const int half = lane >> 5, l32 = lane & 31;
   const bool full = VEC && (m0 + BM <= M) && (n0 + BN <= N);
   if (OUT == 0 && full) {
@@ -1168,15 +1198,16 @@ hipError_t launch_gemm(const void* Aq, const void* As, const void* Bq, const voi
   const auto* b = static_cast<const uint8_t*>(Bq);
   const auto* bs = static_cast<const uint8_t*>(Bs);
   const dim3 blk(256);
-  // Large-tile paths (the main loop runs k-tiles in pairs, so K must hold
-  // an even number of them; 32-bit per-lane operand offsets): 256 x 256
-  // tiles, 8 waves of 128 x 64, with 256-deep k-tiles when K % 512 == 0 and
-  // the scale arrays are 16-byte aligned (scale pairs are 16-byte loads), and
-  // 128-deep ones when only K % 256 == 0 (8-byte pairs).
+  // Large-tile paths (32-bit per-lane operand offsets): 256 x 256 tiles, 8
+  // waves of 128 x 64. The LDS-DMA kernel runs its main loop over 8 k-tiles
+  // of 256 (two scale groups), so it needs K % 2048 == 0 and 16-byte aligned
+  // scale arrays (scale groups are 16-byte loads); the register-staged kernel
+  // runs k-tiles in pairs, 256-deep when K % 512 == 0 (16-byte scale pairs)
+  // and 128-deep when only K % 256 == 0 (8-byte pairs).
   const bool off32 = (M * (K / 2) < (int64_t(1) << 32)) && (N * (K / 2) < (int64_t(1) << 32));
   const bool sc_al = ((uintptr_t)As % 8 == 0) && ((uintptr_t)Bs % 8 == 0);
   const bool sc_al16 = ((uintptr_t)As % 16 == 0) && ((uintptr_t)Bs % 16 == 0);
-  if (off32 && sc_al && K % 512 == 0)
+  if (off32 && sc_al16 && K % 2048 == 0)
     return dm::launch<dm::L<2, 4, 4, 2>>(a, as, b, bs, M, N, K, C, out_dtype, stream);
   if (off32 && sc_al16 && K % 512 == 0)
     return lt::launch<2, 4, 4, 2, 128, 1, 2>(a, as, b, bs, M, N, K, C, out_dtype, stream);

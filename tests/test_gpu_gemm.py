@@ -58,6 +58,10 @@ SHAPES = [
     (300, 200, 512),     # large-tile kernel, ragged M and N
     (1000, 600, 768),    # large-tile kernel, several ragged tiles, odd k-tile pairs
     (768, 1024, 2048),
+    (1, 1, 2048),        # LDS-DMA kernel (K % 2048 == 0), one element
+    (300, 520, 6144),    # LDS-DMA kernel, ragged M and N, three scale-group pairs
+    (257, 261, 2048),    # LDS-DMA kernel, N % 4 != 0 (element-wise epilogue)
+    (513, 260, 8192),    # LDS-DMA kernel, the Wgrad reduction length
 ]
 
 
@@ -81,21 +85,23 @@ def test_gemm_every_scale_byte_in_range():
     check(run_gemm(a, b, M, N, K), a, b, what="wide scales")
 
 
-def test_gemm_zero_and_nan_blocks():
+@pytest.mark.parametrize("K", [256, 2048])
+def test_gemm_zero_and_nan_blocks(K):
     """All-zero operand rows give exact zeros; an E8M0 NaN byte (0xFF)
     poisons exactly the outputs that read that block, as in the oracle."""
-    M, N, K = 64, 96, 256
+    M, N = 64, 96
     a = random_operand(M, K, 5)
     b = random_operand(N, K, 6)
     a[0][3] = 0                # row 3 of A is all zero nibbles
     a[1][5, 2] = 255           # block 2 of A row 5 is NaN
+    a[1][7, K // 32 - 1] = 255  # and the last block of row 7
     C = run_gemm(a, b, M, N, K)
     assert np.all(C[3] == 0)
-    assert np.all(np.isnan(C[5]))
+    assert np.all(np.isnan(C[5])) and np.all(np.isnan(C[7]))
     Cr, _ = O.gemm_ref(O.dequantize(*a), O.dequantize(*b))
     assert np.array_equal(np.isnan(C), np.isnan(Cr))
     keep = np.ones(M, bool)
-    keep[5] = False
+    keep[[5, 7]] = False
     a2 = (a[0][keep], a[1][keep])
     check(C[keep], a2, b, what="rows without NaN")
 
