@@ -15,8 +15,8 @@
 // E8M0 byte of that 32-block in the byte of its scale register picked by
 // op_sel. Output lane l, register r holds C[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32].
 //
-// Three kernels. For K % 2048 == 0 (every Llama-shaped product) the LDS-DMA
-// kernel (namespace dm, below) runs 256 x 256 tiles whose operands go
+// Three kernels. For K % 2048 == 0 (every Llama-shaped product) the persistent
+// LDS-DMA kernel (namespace dm, below) runs 256 x 256 tiles whose operands go
 // straight from global memory to LDS; for K % 256 == 0 the register-staged
 // large-tile kernel (namespace lt) runs the same tiles with 256- or 128-deep
 // k-tiles; both need 32-bit operand offsets. The general kernel here serves
@@ -797,14 +797,19 @@ hipError_t launch(const uint8_t* a, const uint8_t* as, const uint8_t* b, const u
 
 }  // namespace lt
 
-// Large-tile kernel fed by LDS DMA (K % 2048 == 0). Same tile shape and MFMA
-// sequence as gemm_pipe_kernel (256 x 256 tiles, 8 waves of 128 x 64, 256-deep
-// k-tiles, identical operands per MFMA, so identical results); what differs is
-// how operands reach LDS and how C leaves:
+// Persistent large-tile kernel fed by LDS DMA (K % 2048 == 0). One 512-thread
+// work-group per CU walks output tiles t = blockIdx.x, + gridDim.x, ... (256 x
+// 256 tiles, 8 waves of 128 x 64, 4 x 2 MFMA tiles each, 256-deep k-tiles):
 //  * buffer_load_dwordx4 ... lds: the 64 lanes of one instruction write 1 KiB
 //    of LDS at M0 + 16 lane, with no staging registers and no ds_write issued
 //    by the waves that run the MFMAs. A k-tile is 32 such blocks per operand
 //    (8 rows of 128 bytes each), 4 per wave;
+//  * the operand stream does not stop at tile boundaries: the last k-tiles of
+//    one tile prefetch the first k-tiles (and scale groups) of the next, so
+//    no tile starts with an exposed load, and no work-group is relaunched;
+//  * buffer resources start at the tile's first operand row and end at the
+//    operand's end, so the per-lane offsets are the same for every tile and
+//    rows past M or N read as zero (their products are never stored);
 //  * tiles are row-major in LDS (128 bytes per row) with 16-byte chunk c of
 //    row r at slot c ^ ((r >> 1) & 7). The permutation is applied to which
 //    chunk a lane fetches, so a DMA block stays contiguous and 8 lanes fetch a
@@ -822,107 +827,116 @@ hipError_t launch(const uint8_t* a, const uint8_t* as, const uint8_t* b, const u
 //    compiler's wait tracking sees that a DMA into one does not feed reads of
 //    another; a wave waits for its own DMAs (vmcnt) before the barrier that
 //    publishes them;
-//  * full fp32 tiles leave through LDS: a wave writes 32 x 64 of its block at
-//    a time (pitch 68 floats) and stores whole 256-byte row segments with
-//    non-temporal hints. Each store instruction then fills whole cache lines,
-//    and C streams past L2 instead of evicting the operand rows that the next
-//    tiles re-read.
+//  * the MFMA takes A as its first operand, so register r of a lane holds one
+//    C column (lane % 32) of row 8 (r / 4) + 4 (lane / 32) + r % 4: a 4-byte
+//    store of one register writes two whole 128-byte row segments, straight
+//    from the accumulators, non-temporal (C streams past L2 instead of
+//    evicting the operand rows that the next tiles re-read).
 namespace dm {
 
 constexpr int BM = 256, BN = 256;
 constexpr int KB = 128;                      // bytes per operand row per k-tile
 constexpr int TILE = BM * KB;                // 32 KiB per operand
-constexpr int STAGE = 2 * TILE;             // A rows then B rows of one k-tile
-constexpr int SGB = (BM + BN) * 32;         // scale group: 4 k-tiles x 8 bytes per row
+constexpr int STAGE = 2 * TILE;              // A rows then B rows of one k-tile
+constexpr int SGB = (BM + BN) * 32;          // scale group: 4 k-tiles x 8 bytes per row
 
 // Wave layout: WM x WN waves of TM x TN MFMA tiles (TM * 32 x TN * 32 each).
 template <int WM_, int WN_, int TM_, int TN_>
 struct L {
   static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_;
   static constexpr int NW = WM * WN, NT = 64 * NW;
-  static constexpr int DA = 32 / NW;         // 1 KiB DMA blocks per operand per wave
+  static constexpr int DA = 32 / NW;         // 1 KiB data DMA blocks per operand per wave
   static constexpr int DS = 8 / NW;          // 1 KiB scale-group blocks per operand per wave
   static constexpr int NDMA = 2 * DA;        // data DMA instructions per wave per k-tile
-  static constexpr int EP = TN * 32 + 4;     // epilogue staging pitch (floats)
-  static constexpr int ER = 32;              // rows per epilogue pass
   static_assert(WM * TM * 32 == BM && WN * TN * 32 == BN, "256 x 256 tile");
   static_assert(NW * DA == 32 && NW * DS == 8, "DMA blocks divide over the waves");
-  static_assert((NW / 2) * ER * EP * 4 <= STAGE, "half of the waves stage in one stage array");
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 using lt::rsrc_t;
 using lt::u32x2;
 using lt::u32x4;
 
-struct Rsrc {
-  rsrc_t a, b, sa, sb, none;  // none: zero records, every access out of range
+// Buffer resources of one output tile: operand and scale rows from the
+// tile's first row to the operand's last.
+struct TileRes {
+  rsrc_t a, b, sa, sb;
 };
 
-// Per-lane buffer offsets of the thread's DMA rows (rows past M or N clamp to
-// the last row; their products are never stored).
+__device__ __forceinline__ rsrc_t rows_rsrc(const uint8_t* p, int64_t r0, int64_t rows,
+                                            int64_t pitch) {
+  return lt::make_rsrc(p + r0 * pitch, (rows - r0) * pitch);
+}
+
+__device__ __forceinline__ void tile_res(TileRes& T, const uint8_t* A, const uint8_t* As,
+                                         const uint8_t* B, const uint8_t* Bs, int64_t m0,
+                                         int64_t n0, int64_t M, int64_t N, int64_t kbytes,
+                                         int64_t kblk) {
+  T.a = rows_rsrc(A, m0, M, kbytes);
+  T.b = rows_rsrc(B, n0, N, kbytes);
+  T.sa = rows_rsrc(As, m0, M, kblk);
+  T.sb = rows_rsrc(Bs, n0, N, kblk);
+}
+
+// Per-lane DMA offsets within a tile (the same for A and B rows): data block
+// u holds rows 8 u .. 8 u + 7, lane l chunk (l % 8) ^ ((row >> 1) & 7) of row
+// 8 u + l / 8; scale block v holds 32 rows, 16-byte unit l = 32 (r / 16) +
+// 16 s + r % 16 being half s of row r's 32-byte group.
 template <class G>
-struct Dma {
-  uint32_t a[G::DA], b[G::DA], sa[G::DS], sb[G::DS];
+struct Lane {
+  uint32_t d[G::DA], s[G::DS];
 };
 
 template <class G>
-__device__ __forceinline__ void make_dma(Dma<G>& D, int64_t m0, int64_t n0, int64_t M, int64_t N,
-                                         int64_t kbytes, int64_t kblk, int wave, int lane) {
+__device__ __forceinline__ void make_lane(Lane<G>& L, int64_t kbytes, int64_t kblk, int wave,
+                                          int lane) {
 #pragma unroll
   for (int u = 0; u < G::DA; ++u) {
     const int row = 8 * (G::DA * wave + u) + (lane >> 3);
     const int c = (lane & 7) ^ ((row >> 1) & 7);
-    D.a[u] = (uint32_t)(min(m0 + row, M - 1) * kbytes + c * 16);
-    D.b[u] = (uint32_t)(min(n0 + row, N - 1) * kbytes + c * 16);
+    L.d[u] = (uint32_t)(row * kbytes + c * 16);
   }
 #pragma unroll
   for (int v = 0; v < G::DS; ++v) {
     const int srow = 32 * (G::DS * wave + v) + 16 * (lane >> 5) + (lane & 15);
-    const int sh = (lane >> 4) & 1;
-    D.sa[v] = (uint32_t)(min(m0 + srow, M - 1) * kblk + 16 * sh);
-    D.sb[v] = (uint32_t)(min(n0 + srow, N - 1) * kblk + 16 * sh);
+    L.s[v] = (uint32_t)(srow * kblk + 16 * ((lane >> 4) & 1));
   }
 }
 
-// One LDS DMA instruction: lane l's 16 (or 4) bytes at buffer offset
-// voff + soff land at lds + 16 l (or 4 l).
+// One LDS DMA instruction: lane l's 16 bytes at buffer offset voff + soff
+// land at lds + 16 l.
 __device__ __forceinline__ void dma_b128(rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
 }
-__device__ __forceinline__ void dma_b32(rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, soff, 0, 0);
-}
 
-// k-tile kt of this wave's rows into stage st (when live is false every lane
-// is out of range: nothing is read and the stage is never read again).
+// k-tile kt of the tile T into stage st. When live is false every lane reads
+// out of range (nothing is fetched; that stage is never read again).
 template <class G>
-__device__ __forceinline__ void dma_issue(uint8_t* st, const Rsrc& R, const Dma<G>& D, int kt,
-                                          bool live, int wave) {
-  const rsrc_t ra = live ? R.a : R.none, rb = live ? R.b : R.none;
+__device__ __forceinline__ void dma_data(uint8_t* st, const TileRes& T, const Lane<G>& L, int kt,
+                                         bool live, rsrc_t none, int wave) {
+  const rsrc_t ra = live ? T.a : none, rb = live ? T.b : none;
   const uint32_t ko = (uint32_t)kt * KB;
 #pragma unroll
-  for (int u = 0; u < G::DA; ++u) dma_b128(ra, st + (G::DA * wave + u) * 1024, D.a[u], ko);
+  for (int u = 0; u < G::DA; ++u) dma_b128(ra, st + (G::DA * wave + u) * 1024, L.d[u], ko);
 #pragma unroll
-  for (int u = 0; u < G::DA; ++u) dma_b128(rb, st + TILE + (G::DA * wave + u) * 1024, D.b[u], ko);
+  for (int u = 0; u < G::DA; ++u) dma_b128(rb, st + TILE + (G::DA * wave + u) * 1024, L.d[u], ko);
 }
 
-// Scale group g (4 k-tiles, 32 bytes of every scale row) into sg: 1 KiB
-// blocks of 32 rows, unit u = 32 (r / 16) + 16 s + r % 16 holds half s of row r.
+// Scale group g (k-tiles 4 g .. 4 g + 3) of the tile T into sg (A rows, then B rows).
 template <class G>
-__device__ __forceinline__ void dma_scales(uint8_t* sg, const Rsrc& R, const Dma<G>& D, int g,
-                                           bool live, int wave) {
-  const rsrc_t rsa = live ? R.sa : R.none, rsb = live ? R.sb : R.none;
+__device__ __forceinline__ void dma_scales(uint8_t* sg, const TileRes& T, const Lane<G>& L, int g,
+                                           bool live, rsrc_t none, int wave) {
+  const rsrc_t rsa = live ? T.sa : none, rsb = live ? T.sb : none;
   const uint32_t so = (uint32_t)g * 32;
 #pragma unroll
-  for (int v = 0; v < G::DS; ++v) dma_b128(rsa, sg + 1024 * (G::DS * wave + v), D.sa[v], so);
+  for (int v = 0; v < G::DS; ++v) dma_b128(rsa, sg + 1024 * (G::DS * wave + v), L.s[v], so);
 #pragma unroll
-  for (int v = 0; v < G::DS; ++v) dma_b128(rsb, sg + 8192 + 1024 * (G::DS * wave + v), D.sb[v], so);
+  for (int v = 0; v < G::DS; ++v) dma_b128(rsb, sg + 8192 + 1024 * (G::DS * wave + v), L.s[v], so);
 }
 
-// Per-lane LDS read offsets within a stage: fragment of k-step s (chunk
-// 2 s + half of row l32 of each 32-row group), and the lane's scale rows.
+// Per-lane LDS read offsets: fragment of k-step s (chunk 2 s + half of row
+// l32 of each 32-row group) within a stage, and the lane's scale units
+// within a scale group.
 struct RA {
   uint32_t fa[4], fb[4], sa, sb, psel;
 };
@@ -959,6 +973,8 @@ __device__ __forceinline__ void read_frags(const uint8_t* st, const RA& ra,
   }
 }
 
+// Scales of k-tile P (0..3) of a scale group: the row's 8 bytes are half
+// P / 2, word P % 2; the lane keeps the bytes of its 32-element half.
 template <class G, int P>
 __device__ __forceinline__ void read_scales(const uint8_t* sg, const RA& ra,
                                             lt::Scl<G::TM, G::TN>& S) {
@@ -977,6 +993,19 @@ __device__ __forceinline__ void read_scales(const uint8_t* sg, const RA& ra,
   }
 }
 
+// MFMAs of k-step S, A fragment first: accumulator register r of a lane is
+// one C column of one row.
+template <int TM, int TN, int S>
+__device__ __forceinline__ void mfma_ab(const lt::Frag<TM, TN>& F, const lt::Scl<TM, TN>& sc,
+                                          v16f (&acc)[TN][TM]) {
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[i], F.b[j], acc[j][i], 4, 4,
+                                                                  S, sc.a[i], S, sc.b[j]);
+}
+
 // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt at their maxima).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -984,58 +1013,75 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// One k-tile k in stage C (F0 / SCc hold its k-step-0 fragments and its
-// scales). The barrier before the last k-step publishes tile k + 1 (every
-// wave waited for its own DMAs of it) and retires stage C, which then
-// receives tile k + 2 while the last MFMAs of tile k run.
+__device__ __forceinline__ void tile_at(int64_t vt, int64_t ntiles, int64_t ntm, int64_t ntn,
+                                        int64_t& m0, int64_t& n0) {
+  int64_t tm, tn;
+  lt::tile_of<lt::GROUP_M>(vt, ntiles, ntm, ntn, tm, tn);
+  m0 = tm * BM;
+  n0 = tn * BN;
+}
+
+// One k-tile k (C = k % 8) of the current tile, in stage C % 2; F0 / SCc
+// hold its k-step-0 fragments and its scales. The barrier before the last
+// k-step publishes k-tile k + 1 (every wave waited for its own DMAs of it)
+// and retires stage C % 2, which then receives k-tile k + 2 -- of the next
+// tile (Tn) when k + 2 runs past this tile -- while the last MFMAs of k-tile
+// k run. When C % 4 == 3 the scale group buffer of k-tiles k - 3 .. k is
+// retired the same way and receives group (k + 5) / 4.
 template <class G, int C>
 __device__ __forceinline__ void ktile(uint8_t* st0, uint8_t* st1, uint8_t* sg0, uint8_t* sg1,
-                                      const RA& ra, const Rsrc& R,
-                                      const Dma<G>& D, lt::Frag<G::TM, G::TN>& F0,
-                                      lt::Frag<G::TM, G::TN>& F1, const lt::Scl<G::TM, G::TN>& SCc,
-                                      lt::Scl<G::TM, G::TN>& SCn, v16f (&acc)[G::TN][G::TM], int k,
-                                      int nkt, int wave) {
+                                      const RA& ra, const TileRes& Tc, const TileRes& Tn,
+                                      bool has_next, rsrc_t none, const Lane<G>& L,
+                                      lt::Frag<G::TM, G::TN>& F0, lt::Frag<G::TM, G::TN>& F1,
+                                      const lt::Scl<G::TM, G::TN>& SCc, lt::Scl<G::TM, G::TN>& SCn,
+                                      v16f (&acc)[G::TN][G::TM], int k, int nkt, int wave) {
   constexpr int TM = G::TM, TN = G::TN, NM = TM * TN, NR = TM + TN;
+  constexpr bool SG = (C & 3) == 3;
   uint8_t* cur = (C & 1) ? st1 : st0;
   uint8_t* nxt = (C & 1) ? st0 : st1;
-  uint8_t* sgn = (((C + 1) >> 2) & 1) ? sg1 : sg0;   // scale group of tile k + 1
-  uint8_t* sgw = (((C + 5) >> 2) & 1) ? sg1 : sg0;   // group (k + 5) / 4, written when C % 4 == 3
-  constexpr bool SG = (C & 3) == 3;
+  uint8_t* sgn = (((C + 1) >> 2) & 1) ? sg1 : sg0;  // scale group of k-tile k + 1
+  uint8_t* sgw = (((C + 5) >> 2) & 1) ? sg1 : sg0;  // group (k + 5) / 4, written when SG
   read_frags<G, 1>(cur, ra, F1);
-  lt::mfma_step<TM, TN, 0>(F0, SCc, acc);
+  mfma_ab<TM, TN, 0>(F0, SCc, acc);
   lt::interleave<0, NM, NR, 0, 0>();
   __builtin_amdgcn_sched_barrier(0);
   read_frags<G, 2>(cur, ra, F0);
-  lt::mfma_step<TM, TN, 1>(F1, SCc, acc);
+  mfma_ab<TM, TN, 1>(F1, SCc, acc);
   lt::interleave<0, NM, NR, 0, 0>();
   __builtin_amdgcn_sched_barrier(0);
   read_frags<G, 3>(cur, ra, F1);
-  lt::mfma_step<TM, TN, 2>(F0, SCc, acc);
+  mfma_ab<TM, TN, 2>(F0, SCc, acc);
   lt::interleave<0, NM, NR, 0, 0>();
   __builtin_amdgcn_sched_barrier(0);
   wait_vm<0>();
   lt::lds_barrier();
   read_scales<G, (C + 1) & 3>(sgn, ra, SCn);
   read_frags<G, 0>(nxt, ra, F0);
-  dma_issue<G>(cur, R, D, min(k + 2, nkt - 1), k + 2 < nkt, wave);
+  {
+    const int kk = k + 2;
+    const bool nx = kk >= nkt;
+    dma_data<G>(cur, nx ? Tn : Tc, L, nx ? kk - nkt : kk, nx ? has_next : true, none, wave);
+  }
   if constexpr (SG) {
     const int g = (k + 5) >> 2, ng = nkt >> 2;
-    dma_scales<G>(sgw, R, D, min(g, ng - 1), g < ng, wave);
+    const bool nx = g >= ng;
+    dma_scales<G>(sgw, nx ? Tn : Tc, L, nx ? g - ng : g, nx ? has_next : true, none, wave);
   }
-  lt::mfma_step<TM, TN, 3>(F1, SCc, acc);
+  mfma_ab<TM, TN, 3>(F1, SCc, acc);
   lt::interleave<0, NM, 2 * NR, 0, G::NDMA + (SG ? 2 * G::DS : 0)>();
   // the scale byte gathers (v_perm) wait for their reads: keep them last
   __builtin_amdgcn_sched_group_barrier(0x002, NR, 0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <class G, int OUT, bool VEC>
+template <class G, int OUT>
 __global__ __attribute__((amdgpu_flat_work_group_size(G::NT, G::NT),
                           amdgpu_waves_per_eu(G::NW == 8 ? 2 : 1)))
 void gemm_dma_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
                      const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, int64_t M,
                      int64_t N, int64_t K, void* __restrict__ C) {
   constexpr int TM = G::TM, TN = G::TN;
+  constexpr int EB = OUT == 0 ? 4 : 2;  // bytes per C element
   __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sg0[SGB];
@@ -1043,37 +1089,38 @@ void gemm_dma_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave / G::WN, wn = wave % G::WN;
-  const int64_t ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
-  int64_t tm, tn;
-  lt::tile_of<lt::GROUP_M>(blockIdx.x, gridDim.x, ntm, ntn, tm, tn);
-  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int64_t ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN, ntiles = ntm * ntn;
+  const int64_t P = gridDim.x;
   const int64_t kbytes = K / 2, kblk = K / 32;
   const int nkt = (int)(kbytes / KB);
   const int arow0 = wm * TM * 32, brow0 = wn * TN * 32;
-
-  v16f acc[TN][TM];
-#pragma unroll
-  for (int j = 0; j < TN; ++j)
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
-
-  Rsrc R;
-  R.a = lt::make_rsrc(A, M * kbytes);
-  R.b = lt::make_rsrc(B, N * kbytes);
-  R.sa = lt::make_rsrc(As, M * kblk);
-  R.sb = lt::make_rsrc(Bs, N * kblk);
-  R.none = lt::make_rsrc(A, 0);
-  Dma<G> D;
-  make_dma<G>(D, m0, n0, M, N, kbytes, kblk, wave, lane);
+  const rsrc_t none = lt::make_rsrc(A, 0);
   const RA ra = make_ra<G>(wm, wn, lane);
+  Lane<G> L;
+  make_lane<G>(L, kbytes, kblk, wave, lane);
+  // Per-lane part of a full tile's store offsets (the tile's first element
+  // is the store resource's base).
+  const uint32_t vst = (uint32_t)(((int64_t)(arow0 + 4 * half) * N + brow0 + l32) * EB);
+
+  int64_t vt = blockIdx.x;
+  int64_t m0, n0, m0n = 0, n0n = 0;
+  tile_at(vt, ntiles, ntm, ntn, m0, n0);
+  TileRes Tc, Tn;
+  tile_res(Tc, A, As, B, Bs, m0, n0, M, N, kbytes, kblk);
+  bool has_next = vt + P < ntiles;
+  if (has_next) tile_at(vt + P, ntiles, ntm, ntn, m0n, n0n);
+  tile_res(Tn, A, As, B, Bs, m0n, n0n, M, N, kbytes, kblk);
 
   // Prologue: scale group 0, k-tiles 0 and 1, scale group 1 (nkt % 8 == 0).
-  dma_scales<G>(sg0, R, D, 0, true, wave);
-  dma_issue<G>(st0, R, D, 0, true, wave);
-  dma_issue<G>(st1, R, D, 1, true, wave);
-  dma_scales<G>(sg1, R, D, 1, true, wave);
+  // Loads complete in issue order, so this wave's DMAs of group 0 and k-tile
+  // 0 have landed once at most NDMA + 2 DS are outstanding. No LDS reads
+  // precede this barrier, so it needs no release fence (which would also wait
+  // for the later DMAs); the acquire fence keeps the reads below it.
+  dma_scales<G>(sg0, Tc, L, 0, true, none, wave);
+  dma_data<G>(st0, Tc, L, 0, true, none, wave);
+  dma_data<G>(st1, Tc, L, 1, true, none, wave);
+  dma_scales<G>(sg1, Tc, L, 1, true, none, wave);
   wait_vm<G::NDMA + 2 * G::DS>();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -1082,108 +1129,100 @@ void gemm_dma_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   read_scales<G, 0>(sg0, ra, SCa);
   read_frags<G, 0>(st0, ra, F0);
 
-  for (int k = 0; k < nkt; k += 8) {
-    ktile<G, 0>(st0, st1, sg0, sg1, ra, R, D, F0, F1, SCa, SCb, acc, k, nkt, wave);
-    ktile<G, 1>(st0, st1, sg0, sg1, ra, R, D, F0, F1, SCb, SCa, acc, k + 1, nkt, wave);
-    ktile<G, 2>(st0, st1, sg0, sg1, ra, R, D, F0, F1, SCa, SCb, acc, k + 2, nkt, wave);
-    ktile<G, 3>(st0, st1, sg0, sg1, ra, R, D, F0, F1, SCb, SCa, acc, k + 3, nkt, wave);
-    ktile<G, 4>(st0, st1, sg0, sg1, ra, R, D, F0, F1, SCa, SCb, acc, k + 4, nkt, wave);
-    ktile<G, 5>(st0, st1, sg0, sg1, ra, R, D, F0, F1, SCb, SCa, acc, k + 5, nkt, wave);
-    ktile<G, 6>(st0, st1, sg0, sg1, ra, R, D, F0, F1, SCa, SCb, acc, k + 6, nkt, wave);
-    ktile<G, 7>(st0, st1, sg0, sg1, ra, R, D, F0, F1, SCb, SCa, acc, k + 7, nkt, wave);
-  }
-
-  const int half = lane >> 5, l32 = lane & 31;
-  const bool full = VEC && (m0 + BM <= M) && (n0 + BN <= N);
-  if (OUT == 0 && full) {
-    // The last (out-of-range) DMAs wrote into the stages: let them land and
-    // every wave finish its reads before the stages are reused.
-    wait_vm<0>();
-    lt::lds_barrier();
-    constexpr int HW = G::NW / 2, EP = G::EP, ER = G::ER;
-    float* wl = reinterpret_cast<float*>(wave < HW ? st0 : st1) + (wave % HW) * ER * EP;
-    constexpr int LPR = TN * 32 / 4, RPI = 64 / LPR;  // lanes per row segment, rows per store
-    const int rr = lane / LPR, cc = 4 * (lane % LPR);
-#pragma unroll
-    for (int p = 0; p < TM * 32 / ER; ++p) {
-#pragma unroll
-      for (int ii = 0; ii < ER / 32; ++ii) {
-        const int i = p * (ER / 32) + ii;
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<f32x4*>(wl + (ii * 32 + l32) * EP + j * 32 + 8 * q + 4 * half) =
-                f32x4{acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
-                      acc[j][i][4 * q + 3]};
-      }
-#pragma unroll
-      for (int s = 0; s < ER / RPI; ++s) {
-        const int row = s * RPI + rr;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(wl + row * EP + cc);
-        const int64_t m = m0 + arow0 + p * ER + row;
-        __builtin_nontemporal_store(
-            v, reinterpret_cast<f32x4*>(static_cast<float*>(C) + m * N + n0 + brow0 + cc));
-      }
-    }
-    return;
-  }
-  if (full) {  // bf16 out: straight from the accumulators
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int64_t m = m0 + arow0 + i * 32 + l32;
-      uint16_t* p = static_cast<uint16_t*>(C) + m * N + n0 + brow0 + 4 * half;
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t lo = bf16_rne(acc[j][i][4 * q]) | (bf16_rne(acc[j][i][4 * q + 1]) << 16);
-          const uint32_t hi = bf16_rne(acc[j][i][4 * q + 2]) | (bf16_rne(acc[j][i][4 * q + 3]) << 16);
-          *reinterpret_cast<uint2*>(p + j * 32 + 8 * q) = make_uint2(lo, hi);
-        }
-    }
-    return;
-  }
-  // Edge tiles (or unaligned C): element-wise, predicated.
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int64_t m = m0 + arow0 + i * 32 + l32;
+  v16f acc[TN][TM];
+  for (;;) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t n = n0 + brow0 + j * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (m < M && n < N) {
-          if (OUT == 0)
-            static_cast<float*>(C)[m * N + n] = acc[j][i][r];
-          else
-            static_cast<uint16_t*>(C)[m * N + n] = (uint16_t)bf16_rne(acc[j][i][r]);
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
+    for (int k = 0; k < nkt; k += 8) {
+      ktile<G, 0>(st0, st1, sg0, sg1, ra, Tc, Tn, has_next, none, L, F0, F1, SCa, SCb, acc, k, nkt, wave);
+      ktile<G, 1>(st0, st1, sg0, sg1, ra, Tc, Tn, has_next, none, L, F0, F1, SCb, SCa, acc, k + 1, nkt, wave);
+      ktile<G, 2>(st0, st1, sg0, sg1, ra, Tc, Tn, has_next, none, L, F0, F1, SCa, SCb, acc, k + 2, nkt, wave);
+      ktile<G, 3>(st0, st1, sg0, sg1, ra, Tc, Tn, has_next, none, L, F0, F1, SCb, SCa, acc, k + 3, nkt, wave);
+      ktile<G, 4>(st0, st1, sg0, sg1, ra, Tc, Tn, has_next, none, L, F0, F1, SCa, SCb, acc, k + 4, nkt, wave);
+      ktile<G, 5>(st0, st1, sg0, sg1, ra, Tc, Tn, has_next, none, L, F0, F1, SCb, SCa, acc, k + 5, nkt, wave);
+      ktile<G, 6>(st0, st1, sg0, sg1, ra, Tc, Tn, has_next, none, L, F0, F1, SCa, SCb, acc, k + 6, nkt, wave);
+      ktile<G, 7>(st0, st1, sg0, sg1, ra, Tc, Tn, has_next, none, L, F0, F1, SCb, SCa, acc, k + 7, nkt, wave);
+    }
+    // Store the tile: acc[j][i] register r holds
+    // C[m0 + arow0 + 32 i + 8 (r / 4) + 4 half + r % 4][n0 + brow0 + 32 j + l32].
+    if (m0 + BM <= M && n0 + BN <= N) {
+      const rsrc_t rc = lt::make_rsrc(static_cast<uint8_t*>(C) + (m0 * N + n0) * EB,
+                                      min((M - m0) * N * EB, (int64_t)0xffffffff));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t so = (uint32_t)((32 * i + 8 * (r >> 2) + (r & 3)) * N * EB);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            if constexpr (OUT == 0)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j][i][r]), rc,
+                                                    vst + 128 * j, so, 2);
+            else
+              __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne(acc[j][i][r]), rc,
+                                                    vst + 64 * j, so, 2);
+          }
         }
-      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = m0 + arow0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int64_t n = n0 + brow0 + 32 * j + l32;
+            if (m < M && n < N) {
+              if (OUT == 0)
+                static_cast<float*>(C)[m * N + n] = acc[j][i][r];
+              else
+                static_cast<uint16_t*>(C)[m * N + n] = (uint16_t)bf16_rne(acc[j][i][r]);
+            }
+          }
+        }
+    }
+    if (!has_next) break;
+    vt += P;
+    m0 = m0n;
+    n0 = n0n;
+    Tc = Tn;
+    has_next = vt + P < ntiles;
+    if (has_next) {
+      tile_at(vt + P, ntiles, ntm, ntn, m0n, n0n);
+      tile_res(Tn, A, As, B, Bs, m0n, n0n, M, N, kbytes, kblk);
+    }
   }
+  // The last k-tiles' DMAs (out of range) still write LDS: let them land.
+  wait_vm<0>();
+}
+
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, c = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
+      n = c;
+    else
+      n = 256;
+  }
+  return n;
 }
 
 template <class G>
 hipError_t launch(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs,
                   int64_t M, int64_t N, int64_t K, void* C, int out_dtype, hipStream_t stream) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const bool vec = (N % 4 == 0) && ((uintptr_t)C % 16 == 0);
-  const dim3 grid((unsigned)tiles), blk(G::NT);
-  if (out_dtype == 0) {
-    if (vec)
-      hipLaunchKernelGGL((gemm_dma_kernel<G, 0, true>), grid, blk, 0, stream, a, as, b, bs, M, N,
-                         K, C);
-    else
-      hipLaunchKernelGGL((gemm_dma_kernel<G, 0, false>), grid, blk, 0, stream, a, as, b, bs, M,
-                         N, K, C);
-  } else {
-    if (vec)
-      hipLaunchKernelGGL((gemm_dma_kernel<G, 1, true>), grid, blk, 0, stream, a, as, b, bs, M, N,
-                         K, C);
-    else
-      hipLaunchKernelGGL((gemm_dma_kernel<G, 1, false>), grid, blk, 0, stream, a, as, b, bs, M,
-                         N, K, C);
-  }
+  const int64_t ncu = cu_count();
+  const dim3 grid((unsigned)(tiles < ncu ? tiles : ncu)), blk(G::NT);
+  if (out_dtype == 0)
+    hipLaunchKernelGGL((gemm_dma_kernel<G, 0>), grid, blk, 0, stream, a, as, b, bs, M, N, K, C);
+  else
+    hipLaunchKernelGGL((gemm_dma_kernel<G, 1>), grid, blk, 0, stream, a, as, b, bs, M, N, K, C);
   return hipGetLastError();
 }
 
@@ -1199,15 +1238,16 @@ hipError_t launch_gemm(const void* Aq, const void* As, const void* Bq, const voi
   const auto* bs = static_cast<const uint8_t*>(Bs);
   const dim3 blk(256);
   // Large-tile paths (32-bit per-lane operand offsets): 256 x 256 tiles, 8
-  // waves of 128 x 64. The LDS-DMA kernel runs its main loop over 8 k-tiles
-  // of 256 (two scale groups), so it needs K % 2048 == 0 and 16-byte aligned
-  // scale arrays (scale groups are 16-byte loads); the register-staged kernel
+  // waves of 128 x 64. The persistent LDS-DMA kernel runs its main loop over
+  // 8 k-tiles of 256 (two scale groups), so it needs K % 2048 == 0 and
+  // 16-byte aligned scale arrays (scale groups are 16-byte loads), and its
+  // 32-bit store offsets span 256 rows of C (N < 2^22); the register-staged kernel
   // runs k-tiles in pairs, 256-deep when K % 512 == 0 (16-byte scale pairs)
   // and 128-deep when only K % 256 == 0 (8-byte pairs).
   const bool off32 = (M * (K / 2) < (int64_t(1) << 32)) && (N * (K / 2) < (int64_t(1) << 32));
   const bool sc_al = ((uintptr_t)As % 8 == 0) && ((uintptr_t)Bs % 8 == 0);
   const bool sc_al16 = ((uintptr_t)As % 16 == 0) && ((uintptr_t)Bs % 16 == 0);
-  if (off32 && sc_al16 && K % 2048 == 0)
+  if (off32 && sc_al16 && K % 2048 == 0 && N < (int64_t(1) << 22))
     return dm::launch<dm::L<2, 4, 4, 2>>(a, as, b, bs, M, N, K, C, out_dtype, stream);
   if (off32 && sc_al16 && K % 512 == 0)
     return lt::launch<2, 4, 4, 2, 128, 1, 2>(a, as, b, bs, M, N, K, C, out_dtype, stream);
