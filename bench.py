@@ -241,8 +241,10 @@ def main():
     ap.add_argument("--quant-iters", type=int, default=50)
     ap.add_argument("--no-error-report", action="store_true")
     ap.add_argument("--pmc-gemm", action="store_true",
-                    help="counter-collection mode: run only the gate+up GEMM (3 launches) and a "
-                         "1 GiB device-to-device copy (3 launches, the calibration kernel)")
+                    help="counter-collection mode: run only the gate+up GEMM (3 launches), the "
+                         "row and column H16 quantizers on the 8192x4096 workload (3 launches "
+                         "each) and a 1 GiB device-to-device copy (3 launches, the calibration "
+                         "kernel)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -273,13 +275,18 @@ def main():
         c = torch.empty((8192, 28672), dtype=torch.float32, device=dev)
         for _ in range(3):
             mx.mxfp4_gemm(an, asc, bn, bsc, 8192, 28672, 4096, c, mx.OUT_F32, stream)
+        del c
+        q = torch.from_numpy(synthetic.make("quant")["A"].view(np.int16)).to(dev).view(torch.bfloat16)
+        for axis in (mx.AXIS_ROW, mx.AXIS_COL):
+            for _ in range(3):
+                mx.quantize(q, axis, 16, 0)
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         src.fill_(1)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        log("pmc-gemm done: 3 gate+up GEMMs, 3 copies of 1 GiB")
+        log("pmc-gemm done: 3 gate+up GEMMs, 3 row + 3 column quantizations, 3 copies of 1 GiB")
         return
 
     # ---------------------------------------------------------------- inputs

@@ -9,13 +9,18 @@ counter columns of a ``*_counter_collection.csv`` per (kernel, grid).
 
 usage: python profile_summary.py TRACE_CSV [--pmc COUNTER_CSV]
        python profile_summary.py --traffic FETCH_CSV WRITE_CSV KERNEL_SRC OUT_JSON
+       python profile_summary.py --traffic-md FETCH_CSV WRITE_CSV OUT_MD [--command CMD]
+       python profile_summary.py --mfma COUNTER_CSV OUT_MD [--command CMD]
 
 --traffic turns two counter runs of `bench.py --pmc-gemm` (FETCH_SIZE, then
 WRITE_SIZE, in KiB per dispatch) into HBM bytes per GEMM launch. Each counter
 is scaled by bytes / counter of the 1 GiB copy kernel in the same run (the
 copy reads and writes exactly 2^30 bytes), and the result is written with
 the sha256 of the kernel source's code (comments and blank lines dropped)
-it was measured on.
+it was measured on. --traffic-md writes the same calibrated bytes for every
+kernel of the run (GEMM and quantizers) as a markdown table, and --mfma
+turns a GRBM_GUI_ACTIVE / SQ_VALU_MFMA_BUSY_CYCLES / TA_TA_BUSY_sum run into
+MFMA utilisation and effective clock per GEMM launch.
 """
 from __future__ import annotations
 
@@ -90,6 +95,88 @@ def sha_of(path):
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
+def _per_launch(path, counter):
+    """Counter values per (kernel, grid size) launch shape."""
+    out = defaultdict(list)
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter:
+                grid = int(row.get("Grid_Size") or row.get("Grid_Size_X"))
+                out[(short(row["Kernel_Name"]), grid)].append(float(row["Counter_Value"]))
+    return out
+
+
+# Algorithmic bytes of the launch shapes that bench.py --pmc-gemm runs:
+# the 8192 x 4096 quantizer workload (2 B read + 0.5 B nibbles + 1/32 B
+# scale per element) and the gate+up GEMM (packed operands + fp32 C).
+QUANT_BYTES = 8192 * 4096 * 2 + 8192 * 4096 // 2 + 8192 * 4096 // 32
+GEMM_BYTES = 8192 * 2048 + 8192 * 128 + 28672 * 2048 + 28672 * 128 + 8192 * 28672 * 4
+
+
+def traffic_table(fetch_csv, write_csv, out_md, command):
+    """Markdown table: HBM-side read/write bytes per launch of every kernel
+    in a --pmc-gemm run, calibrated on the 1 GiB copy."""
+    fetch = _per_launch(fetch_csv, "FETCH_SIZE")
+    write = _per_launch(write_csv, "WRITE_SIZE")
+    ck = [k for k in fetch if "copyBuffer" in k[0] and k in write]
+    ck = max(ck, key=lambda k: sum(fetch[k]) / len(fetch[k]))
+    f_factor = float(1 << 30) / (sum(fetch[ck]) / len(fetch[ck]) * 1024.0)
+    w_factor = float(1 << 30) / (sum(write[ck]) / len(write[ck]) * 1024.0)
+    lines = ["| kernel | grid | dispatches | read MB | write MB | total MB | algorithmic MB |",
+             "|---|---|---|---|---|---|---|"]
+    for key in fetch:
+        if key not in write or key == ck:
+            continue
+        rd = sum(fetch[key]) / len(fetch[key]) * 1024.0 * f_factor
+        wr = sum(write[key]) / len(write[key]) * 1024.0 * w_factor
+        alg = GEMM_BYTES if "gemm" in key[0] else (QUANT_BYTES if "quant" in key[0] else None)
+        lines.append(f"| {key[0]} | {key[1]} | {len(fetch[key])} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | "
+                     f"{(rd + wr) / 1e6:.1f} | {alg / 1e6 if alg else float('nan'):.1f} |")
+    text = ("# HBM-side traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)\n\n"
+            f"Calibration: {ck[0]} copying 1 GiB; FETCH_SIZE x {f_factor:.3f}, WRITE_SIZE x "
+            f"{w_factor:.3f} give its 2^30 read and written bytes. FETCH_SIZE and WRITE_SIZE "
+            "count L2-to-fabric bytes (HBM or the Infinity Cache in front of it).\n\n"
+            f"Command (from /tmp, TMPDIR=/tmp, repository at $R):\n\n    {command}\n\n"
+            + "\n".join(lines) + "\n")
+    with open(out_md, "w") as f:
+        f.write(text)
+    print(text)
+
+
+def mfma_table(csv_path, out_md, command, xcds=8, simds=1024):
+    """MFMA utilisation and effective clock per GEMM launch shape from a run
+    with GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES (GRBM_GUI_ACTIVE is
+    summed over the XCDs; SQ_VALU_MFMA_BUSY_CYCLES over every SIMD)."""
+    per = defaultdict(lambda: defaultdict(float))
+    meta = {}
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            d = int(row["Dispatch_Id"])
+            per[d][row["Counter_Name"]] += float(row["Counter_Value"])
+            meta[d] = (short(row["Kernel_Name"]), int(row.get("Grid_Size") or row.get("Grid_Size_X")),
+                       (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
+    lines = ["| kernel | grid | dispatch | us | clock GHz | MFMA busy % | TA busy % |",
+             "|---|---|---|---|---|---|---|"]
+    for d in sorted(per):
+        k, g, us = meta[d]
+        c = per[d]
+        gui = c.get("GRBM_GUI_ACTIVE", 0.0) / xcds
+        if not gui or "SQ_VALU_MFMA_BUSY_CYCLES" not in c:
+            continue
+        mf = 100.0 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * simds)
+        ta = 100.0 * c.get("TA_TA_BUSY_sum", float("nan")) / (gui * simds / 4)
+        lines.append(f"| {k} | {g} | {d} | {us:.1f} | {gui / us / 1e3:.2f} | {mf:.1f} | {ta:.1f} |")
+    text = ("# MFMA utilisation of the GEMM launches (rocprofv3 counters)\n\n"
+            "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
+            "TA busy = TA_TA_BUSY summed over CUs / (GRBM_GUI_ACTIVE / 8 x 256 CUs); clock = "
+            "GRBM_GUI_ACTIVE / 8 / kernel duration.\n\n"
+            f"Command (from /tmp, TMPDIR=/tmp, repository at $R):\n\n    {command}\n\n"
+            + "\n".join(lines) + "\n")
+    with open(out_md, "w") as f:
+        f.write(text)
+    print(text)
+
+
 def traffic(fetch_csv, write_csv, kernel_src, out_json):
     import json
     fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
@@ -121,6 +208,9 @@ if __name__ == "__main__":
     ap.add_argument("trace", nargs="?")
     ap.add_argument("--pmc")
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL_SRC", "OUT_JSON"))
+    ap.add_argument("--traffic-md", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"))
+    ap.add_argument("--mfma", nargs=2, metavar=("COUNTER_CSV", "OUT_MD"))
+    ap.add_argument("--command", default="", help="command line recorded in the markdown")
     a = ap.parse_args()
     if a.trace:
         trace_summary(a.trace)
@@ -128,3 +218,7 @@ if __name__ == "__main__":
         pmc_summary(a.pmc)
     if a.traffic:
         traffic(*a.traffic)
+    if a.traffic_md:
+        traffic_table(*a.traffic_md, a.command)
+    if a.mfma:
+        mfma_table(*a.mfma, a.command)
