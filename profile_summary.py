@@ -47,18 +47,36 @@ def short(name: str) -> str:
     return out
 
 
+# The persistent GEMM launches one work-group per CU for every shape, so its
+# grid does not identify the product; the quantizer launch just before it
+# does (its B operand: grid = blocks of the weight or the column source).
+PRODUCT_OF_B_GRID = {786432: "qkv fprop (8192,6144,4096)",
+                     3670016: "gate+up fprop (8192,28672,4096)",
+                     458752: "down dgrad (8192,14336,4096)",
+                     917504: "down wgrad (4096,14336,8192)"}
+
+
 def trace_summary(path):
     groups = defaultdict(list)
     with open(path) as f:
-        for row in csv.DictReader(f):
-            key = (short(row["Kernel_Name"]), int(row["Grid_Size_X"]) * int(row["Grid_Size_Y"]) *
-                   int(row["Grid_Size_Z"]), int(row["Workgroup_Size_X"]))
-            dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
-            groups[key].append(dur)
-    print("| kernel | grid threads | wg | calls | avg us | min us | max us |")
-    print("|---|---|---|---|---|---|---|")
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    prev = None
+    for row in rows:
+        name = short(row["Kernel_Name"])
+        grid = int(row["Grid_Size_X"]) * int(row["Grid_Size_Y"]) * int(row["Grid_Size_Z"])
+        key = (name, grid, int(row["Workgroup_Size_X"]))
+        if name.startswith("gemm_dma_kernel") and prev is not None:
+            key = (f"{name} [{PRODUCT_OF_B_GRID.get(prev[1], 'after ' + prev[0])}]", grid, key[2])
+        dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+        groups[key].append(dur)
+        if name.startswith("quant"):
+            prev = (name, grid)
+    print("| kernel | grid threads | wg | calls | avg us | median us | min us | max us |")
+    print("|---|---|---|---|---|---|---|---|")
     for (k, g, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-        print(f"| {k} | {g} | {wg} | {len(d)} | {sum(d) / len(d):.2f} | {min(d):.2f} | {max(d):.2f} |")
+        med = sorted(d)[len(d) // 2]
+        print(f"| {k} | {g} | {wg} | {len(d)} | {sum(d) / len(d):.2f} | {med:.2f} | {min(d):.2f} | "
+              f"{max(d):.2f} |")
 
 
 def pmc_summary(path):
@@ -106,10 +124,10 @@ def _per_launch(path, counter):
     return out
 
 
-# Algorithmic bytes of the launch shapes that bench.py --pmc-gemm runs:
-# the 8192 x 4096 quantizer workload (2 B read + 0.5 B nibbles + 1/32 B
-# scale per element) and the gate+up GEMM (packed operands + fp32 C).
-QUANT_BYTES = 8192 * 4096 * 2 + 8192 * 4096 // 2 + 8192 * 4096 // 32
+# Algorithmic bytes of the launch shapes that bench.py --pmc-gemm runs: the
+# quantizers (2 B read + 0.5 B nibbles + 1/32 B scale per element) and the
+# gate+up GEMM (packed operands + fp32 C).
+QUANT_PER_ELEMENT = 2 + 0.5 + 1 / 32
 GEMM_BYTES = 8192 * 2048 + 8192 * 128 + 28672 * 2048 + 28672 * 128 + 8192 * 28672 * 4
 
 
@@ -129,7 +147,11 @@ def traffic_table(fetch_csv, write_csv, out_md, command):
             continue
         rd = sum(fetch[key]) / len(fetch[key]) * 1024.0 * f_factor
         wr = sum(write[key]) / len(write[key]) * 1024.0 * w_factor
-        alg = GEMM_BYTES if "gemm" in key[0] else (QUANT_BYTES if "quant" in key[0] else None)
+        alg = GEMM_BYTES if "gemm" in key[0] else None
+        if key[0].startswith("quant_row_kernel"):      # one thread per 32-element block
+            alg = key[1] * 32 * QUANT_PER_ELEMENT
+        elif key[0].startswith("quant_col_staged"):   # one thread per 4 x 32 patch
+            alg = key[1] * 128 * QUANT_PER_ELEMENT
         lines.append(f"| {key[0]} | {key[1]} | {len(fetch[key])} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | "
                      f"{(rd + wr) / 1e6:.1f} | {alg / 1e6 if alg else float('nan'):.1f} |")
     text = ("# HBM-side traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)\n\n"
@@ -161,7 +183,7 @@ def mfma_table(csv_path, out_md, command, xcds=8, simds=1024):
         k, g, us = meta[d]
         c = per[d]
         gui = c.get("GRBM_GUI_ACTIVE", 0.0) / xcds
-        if not gui or "SQ_VALU_MFMA_BUSY_CYCLES" not in c:
+        if not gui or "SQ_VALU_MFMA_BUSY_CYCLES" not in c or "gemm" not in k:
             continue
         mf = 100.0 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * simds)
         ta = 100.0 * c.get("TA_TA_BUSY_sum", float("nan")) / (gui * simds / 4)
