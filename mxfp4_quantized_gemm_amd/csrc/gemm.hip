@@ -856,6 +856,7 @@ struct L {
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 using lt::rsrc_t;
 using lt::u32x2;
 using lt::u32x4;
@@ -1194,8 +1195,9 @@ void gemm_dma_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
                                                                         0xf, false);
                 const float lo = __uint_as_float(odd ? rcv : a), hi = __uint_as_float(odd ? b : rcv);
                 const uint32_t so = (uint32_t)((32 * i + 8 * q + e + 4 * t) * N * 2);
-                __builtin_amdgcn_raw_buffer_store_b32(bf16_rne(lo) | (bf16_rne(hi) << 16), rc, vb,
-                                                      so, 2);
+                const bf16x2 pk = {(__bf16)lo, (__bf16)hi};  // v_cvt_pk_bf16_f32 (RNE)
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pk), rc, vb, so,
+                                                      2);
               }
             }
       }
