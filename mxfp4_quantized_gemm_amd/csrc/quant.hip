@@ -23,6 +23,23 @@
 namespace mx {
 namespace {
 
+// Non-temporal loads of a lane's 8 or 16 consecutive source bytes. Every
+// kernel reads its source once; where the 64 lanes of a load read one
+// contiguous row segment, the non-temporal hint is 10-16% faster (measured on
+// the column kernels: 8192 x 4096 20.1 -> 17.1 us, 8192 x 14336 68.5 -> 57.8
+// us), while on a lane-strided pattern it is slower, so only contiguous
+// loads use it.
+typedef unsigned int nt_u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 ld_nt8(const uint16_t* p) {
+  const nt_u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x2*>(p));
+  return make_uint2(w.x, w.y);
+}
+__device__ __forceinline__ uint4 ld_nt16(const uint16_t* p) {
+  const nt_u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+  return make_uint4(w.x, w.y, w.z, w.w);
+}
+
 // ---------------------------------------------------------------- row (1x32)
 // One thread per 32-element block of a row-major matrix whose rows are a
 // multiple of 32 long, so block b covers elements [32b, 32b + 32) of the
@@ -37,6 +54,70 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const uint4* __restrict_
   uint4 q[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) q[j] = src[b * 4 + j];
+  float v[32];
+  unpack64B(q, v);
+  hadamard32<H>(v);
+  uint4 out;
+  uint32_t s;
+  encode_block<MODE>(v, out, s);
+  nib[b] = out;
+  sc[b] = (uint8_t)s;
+}
+
+// Lane-contiguous variant (nblocks % 64 == 0): a wave owns 64 consecutive
+// blocks (4 KiB of bf16) and reads them with four 1 KiB instructions, lane l
+// of instruction j taking 16-byte chunk 64 j + l (block 16 j + l / 4,
+// quarter l % 4), so that every instruction covers whole cache lines once.
+// A 4 x 4 transpose inside each lane quad (two DPP exchange stages, per
+// dword) then gives lane 4 Q + p the four quarters of block 16 p + Q. The
+// loads are non-temporal: the source is read once. Measured against the
+// one-block-per-thread kernel (each load of which touches every line of a
+// 4 KiB span a quarter at a time): 8192 x 28672 104 -> 89 us (6.7 TB/s),
+// 32768 x 8192 119 -> 115 us, 8192 x 4096 16.7 -> 17.5 us; used above
+// 2^20 blocks.
+template <int CTRL>
+__device__ __forceinline__ uint32_t quad_swap(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ void quad_transpose(uint32_t (&x)[4], int p) {
+  const bool b1 = (p & 2) != 0, b0 = (p & 1) != 0;
+  // stage 1: lanes p and p ^ 2 trade a pair of values (quad_perm [2,3,0,1])
+  const uint32_t r0 = quad_swap<0x4e>(b1 ? x[0] : x[2]), r1 = quad_swap<0x4e>(b1 ? x[1] : x[3]);
+  if (b1) { x[0] = r0; x[1] = r1; } else { x[2] = r0; x[3] = r1; }
+  // stage 2: lanes p and p ^ 1 trade one value of each pair (quad_perm [1,0,3,2])
+  const uint32_t u0 = quad_swap<0xb1>(b0 ? x[0] : x[1]), u1 = quad_swap<0xb1>(b0 ? x[2] : x[3]);
+  if (b0) { x[0] = u0; x[2] = u1; } else { x[1] = u0; x[3] = u1; }
+}
+
+template <int H, int MODE>
+__global__ __launch_bounds__(256) void quant_row_lc_kernel(const uint4* __restrict__ src,
+                                                           uint4* __restrict__ nib,
+                                                           uint8_t* __restrict__ sc) {
+  const int lane = threadIdx.x & 63;
+  const int64_t b0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;
+  const nt_u32x4* s4 = reinterpret_cast<const nt_u32x4*>(src);
+  uint4 q[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const nt_u32x4 w = __builtin_nontemporal_load(s4 + b0 * 4 + 64 * j + lane);
+    q[j] = make_uint4(w.x, w.y, w.z, w.w);
+  }
+  const int p = lane & 3;
+  uint32_t x[4];
+  x[0] = q[0].x; x[1] = q[1].x; x[2] = q[2].x; x[3] = q[3].x;
+  quad_transpose(x, p);
+  q[0].x = x[0]; q[1].x = x[1]; q[2].x = x[2]; q[3].x = x[3];
+  x[0] = q[0].y; x[1] = q[1].y; x[2] = q[2].y; x[3] = q[3].y;
+  quad_transpose(x, p);
+  q[0].y = x[0]; q[1].y = x[1]; q[2].y = x[2]; q[3].y = x[3];
+  x[0] = q[0].z; x[1] = q[1].z; x[2] = q[2].z; x[3] = q[3].z;
+  quad_transpose(x, p);
+  q[0].z = x[0]; q[1].z = x[1]; q[2].z = x[2]; q[3].z = x[3];
+  x[0] = q[0].w; x[1] = q[1].w; x[2] = q[2].w; x[3] = q[3].w;
+  quad_transpose(x, p);
+  q[0].w = x[0]; q[1].w = x[1]; q[2].w = x[2]; q[3].w = x[3];
+  const int64_t b = b0 + 16 * p + (lane >> 2);
   float v[32];
   unpack64B(q, v);
   hadamard32<H>(v);
@@ -119,7 +200,7 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
   const uint16_t* p = src + band * 32 * cols + c0;
   uint4 raw[32];
 #pragma unroll
-  for (int r = 0; r < 32; ++r) raw[r] = *reinterpret_cast<const uint4*>(p + r * cols);
+  for (int r = 0; r < 32; ++r) raw[r] = ld_nt16(p + r * cols);
   const int64_t nib_pitch = rows / 2, sc_pitch = rows / 32;
 #pragma unroll
   for (int pr = 0; pr < 4; ++pr) {
@@ -171,7 +252,7 @@ __global__ __launch_bounds__(64 * NB) void quant_col_staged_kernel(const uint16_
     const uint16_t* p = src + band * 32 * cols + c0;
     uint2 raw[32];
 #pragma unroll
-    for (int r = 0; r < 32; ++r) raw[r] = *reinterpret_cast<const uint2*>(p + r * cols);
+    for (int r = 0; r < 32; ++r) raw[r] = ld_nt8(p + r * cols);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {  // one column at a time keeps the register count low
       float a[32];
@@ -322,7 +403,7 @@ __global__ __launch_bounds__(64 * NB) void quant_dual_kernel(const uint16_t* __r
   const uint16_t* p = src + band * 32 * cols + c0;
   uint2 raw[32];
 #pragma unroll
-  for (int r = 0; r < 32; ++r) raw[r] = *reinterpret_cast<const uint2*>(p + r * cols);
+  for (int r = 0; r < 32; ++r) raw[r] = ld_nt8(p + r * cols);
   // row direction
 #pragma unroll
   for (int r = 0; r < 32; ++r) {
@@ -611,9 +692,17 @@ hipError_t dispatch_axis(const void* src, int64_t rows, int64_t cols, int axis, 
   if (axis == 0) {
     const int64_t nblocks = rows * (cols / 32);
     const int64_t grid = (nblocks + 255) / 256;
-    hipLaunchKernelGGL((quant_row_kernel<H, MODE>), dim3((unsigned)grid), blk, 0, st,
-                       static_cast<const uint4*>(src), nblocks, static_cast<uint4*>(nib),
-                       static_cast<uint8_t*>(sc));
+    // The lane-contiguous kernel wins on large tensors; on 8192 x 4096 and
+    // below, and inside the Llama step (after a GEMM), the one-block-per-
+    // thread kernel was as fast or faster (in-step A/B: 17.5 vs 20.5 us).
+    if (nblocks % 256 == 0 && nblocks > (int64_t(1) << 20))
+      hipLaunchKernelGGL((quant_row_lc_kernel<H, MODE>), dim3((unsigned)grid), blk, 0, st,
+                         static_cast<const uint4*>(src), static_cast<uint4*>(nib),
+                         static_cast<uint8_t*>(sc));
+    else
+      hipLaunchKernelGGL((quant_row_kernel<H, MODE>), dim3((unsigned)grid), blk, 0, st,
+                         static_cast<const uint4*>(src), nblocks, static_cast<uint4*>(nib),
+                         static_cast<uint8_t*>(sc));
   } else if (axis == 1) {
     if (rows % 256 == 0 && cols % 4 == 0 && ((uintptr_t)sc % 8 == 0)) {
       const int64_t grid = (rows / 256) * ((cols + 255) / 256);

@@ -135,6 +135,15 @@ def test_quantizer_workload_full_size_other_rotations(quant_workload, h):
     assert_same(quant_workload, 0, h, 0, f"full row h={h}")
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_row_quantizer_above_lane_contiguous_threshold(quant_workload, mode):
+    """Row-wise quantization of more than 2^20 blocks runs the lane-contiguous
+    kernel (quad-transposed loads): 8448 x 4096 (the workload plus its first
+    256 rows again), every byte."""
+    big = np.concatenate([quant_workload, quant_workload[:256]], axis=0)
+    assert_same(big, AXES["row"], 16, mode, f"row 8448x4096 mode={mode}")
+
+
 # ------------------------------------------------------- dual orientation
 def run_gpu_dual(bits, h, mode):
     import torch
