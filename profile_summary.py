@@ -148,7 +148,7 @@ def traffic_table(fetch_csv, write_csv, out_md, command):
         rd = sum(fetch[key]) / len(fetch[key]) * 1024.0 * f_factor
         wr = sum(write[key]) / len(write[key]) * 1024.0 * w_factor
         alg = GEMM_BYTES if "gemm" in key[0] else None
-        if key[0].startswith("quant_row_kernel"):      # one thread per 32-element block
+        if key[0].startswith("quant_row"):             # one thread per 32-element block
             alg = key[1] * 32 * QUANT_PER_ELEMENT
         elif key[0].startswith("quant_col_staged"):   # one thread per 4 x 32 patch
             alg = key[1] * 128 * QUANT_PER_ELEMENT
