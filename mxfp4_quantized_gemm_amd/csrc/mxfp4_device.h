@@ -107,5 +107,91 @@ __device__ __forceinline__ void encode_block(const float (&v)[32], uint4& nib, u
   nib = (s == 255u) ? make_uint4(0, 0, 0, 0) : encode32(v, scale_of_byte(s));
 }
 
+// ------------------------------------------ H16 with the 1/4 folded into E
+// The H16 normalisation 1/4 is a power of two, so it can move from the
+// values into the scale: with u the unnormalised butterfly output and
+// y = u / 4, every finite |u| is a multiple of 2^-133 (a bf16 quantum)
+// and below 2^128, so y is exact (a non-finite u gives the same 0xFF block
+// either way), amax(y) = amax(u) / 4 exactly, and
+// code(y / 2^E) = code(u / 2^(E+2)). Kernels that quantize without keeping
+// y therefore skip the multiply (one VALU op per element) and use the
+// helpers below with SH = 2 (SH = 0 for H32 and H0, whose values are the
+// rotated values themselves). The result is bit-identical to the
+// normalise-then-quantize order.
+template <int H>
+constexpr int kScaleShift = (H == 16) ? 2 : 0;
+
+// E8M0 byte of a block whose stored values are 2^SH times the rotated
+// values and whose stored amax has fp32 bits `a`. With SH = 2 the amax of
+// the rotated values is a / 4: its exponent is two lower (or it is
+// subnormal and lands on the clamp, as does every e <= -127 here) and its
+// mantissa is unchanged, so the e8m0_byte rules apply to the shifted
+// exponent.
+template <int MODE, int SH>
+__device__ __forceinline__ uint32_t e8m0_byte_sh(uint32_t a) {
+  if (a >= 0x7f800000u) return 255u;
+  int E = (int)(a >> 23) - 129 - SH;
+  if (MODE == kCeil && (a & 0x7fffffu) > 0x400000u) E += 1;
+  E = max(E, -127);
+  return (uint32_t)(E + 127);
+}
+
+// The convert's divisor for byte s of values stored at 2^SH times their
+// rotated value: 2^(s - 127 + SH). With SH = 2 and finite stored values the
+// byte is at most 251, so the divisor is a normal fp32 power of two.
+template <int SH>
+__device__ __forceinline__ float cvt_scale(uint32_t s) {
+  if constexpr (SH == 0)
+    return scale_of_byte(s);
+  else
+    return __uint_as_float((s + SH) << 23);
+}
+
+// Butterfly of hadamard32 with H32's multiply but without H16's 1/4.
+template <int H>
+__device__ __forceinline__ void butterfly32(float (&v)[32]) {
+  if constexpr (H != 0) {
+#pragma unroll
+    for (int s = 1; s < H; s <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if ((i & s) == 0) {
+          const float a = v[i], b = v[i + s];
+          v[i] = a + b;
+          v[i + s] = a - b;
+        }
+      }
+    }
+    if constexpr (H == 32) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] *= __uint_as_float(0x3E3504F3u);
+    }
+  }
+}
+
+// Largest |v| of N values as fp32 bits, ordered as amax_bits32 (NaN above
+// +Inf above every finite value) with one three-input max per two values
+// and no sign masking per value: the unsigned max of the raw bits is the
+// largest negative magnitude (sign bit set) whenever a value is negative,
+// the signed max (floored at 0) the largest non-negative one.
+template <int N>
+__device__ __forceinline__ uint32_t amax_bits_n(const float* v) {
+  uint32_t mu = 0;
+  int32_t mi = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    mu = max(mu, __float_as_uint(v[i]));
+    mi = max(mi, (int32_t)__float_as_uint(v[i]));
+  }
+  return max(mu & 0x7fffffffu, (uint32_t)mi);
+}
+
+// encode_block for values stored at 2^SH times their rotated value.
+template <int MODE, int SH>
+__device__ __forceinline__ void encode_block_sh(const float (&v)[32], uint4& nib, uint32_t& s) {
+  s = e8m0_byte_sh<MODE, SH>(amax_bits_n<32>(v));
+  nib = (s == 255u) ? make_uint4(0, 0, 0, 0) : encode32(v, cvt_scale<SH>(s));
+}
+
 }  // namespace
 }  // namespace mx

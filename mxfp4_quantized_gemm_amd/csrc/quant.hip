@@ -11,9 +11,11 @@
 // Every kernel is HBM-bound: it reads 2 B/element of bf16 and writes
 // 0.5 B/element of packed E2M1 plus one E8M0 byte per block. Per element the
 // ALU work is the widening shift, the fp32 butterfly (log2 h add/sub), one
-// multiply by the Hadamard normalisation, an integer max for the block amax
-// and half of one v_cvt_scalef32_pk_fp4_f32 (gfx950's scaled FP4 convert,
-// which rounds x / 2^E to nearest-even E2M1 and saturates at 6).
+// multiply by the Hadamard normalisation (H32 only: H16's 1/4 is folded into
+// the convert's power-of-two divisor, bit-identically), an integer max for
+// the block amax and half of one v_cvt_scalef32_pk_fp4_f32 (gfx950's scaled
+// FP4 convert, which rounds x / 2^E to nearest-even E2M1 and saturates at
+// 6).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -56,10 +58,10 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const uint4* __restrict_
   for (int j = 0; j < 4; ++j) q[j] = src[b * 4 + j];
   float v[32];
   unpack64B(q, v);
-  hadamard32<H>(v);
+  butterfly32<H>(v);
   uint4 out;
   uint32_t s;
-  encode_block<MODE>(v, out, s);
+  encode_block_sh<MODE, kScaleShift<H>>(v, out, s);
   nib[b] = out;
   sc[b] = (uint8_t)s;
 }
@@ -120,10 +122,10 @@ __global__ __launch_bounds__(256) void quant_row_lc_kernel(const uint4* __restri
   const int64_t b = b0 + 16 * p + (lane >> 2);
   float v[32];
   unpack64B(q, v);
-  hadamard32<H>(v);
+  butterfly32<H>(v);
   uint4 out;
   uint32_t s;
-  encode_block<MODE>(v, out, s);
+  encode_block_sh<MODE, kScaleShift<H>>(v, out, s);
   nib[b] = out;
   sc[b] = (uint8_t)s;
 }
@@ -154,12 +156,12 @@ __global__ __launch_bounds__(256) void quant_2d_kernel(const uint16_t* __restric
 #pragma unroll
     for (int j = 0; j < 4; ++j) q[j] = p[j];
     unpack64B(q, v);
-    hadamard32<H>(v);
+    butterfly32<H>(v);
   } else {
 #pragma unroll
     for (int i = 0; i < 32; ++i) v[i] = 0.f;
   }
-  uint32_t am = amax_bits32(v);
+  uint32_t am = amax_bits_n<32>(v);
   am = max(am, (uint32_t)__shfl_xor((int)am, 8));
   am = max(am, (uint32_t)__shfl_xor((int)am, 16));
   am = max(am, (uint32_t)__shfl_xor((int)am, 32));
@@ -168,8 +170,8 @@ __global__ __launch_bounds__(256) void quant_2d_kernel(const uint16_t* __restric
   __syncthreads();
   am = max(max(red[0][cbl], red[1][cbl]), max(red[2][cbl], red[3][cbl]));
   if (!active) return;
-  const uint32_t s = e8m0_byte<MODE>(am);
-  const uint4 out = (s == 255u) ? make_uint4(0, 0, 0, 0) : encode32(v, scale_of_byte(s));
+  const uint32_t s = e8m0_byte_sh<MODE, kScaleShift<H>>(am);
+  const uint4 out = (s == 255u) ? make_uint4(0, 0, 0, 0) : encode32(v, cvt_scale<kScaleShift<H>>(s));
   reinterpret_cast<uint4*>(nib + row * (cols / 2))[cb] = out;
   if (r == 0) sc[tile_row * ncb + cb] = (uint8_t)s;
 }
@@ -211,12 +213,12 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
       a[r] = bf16lo(d);
       b[r] = bf16hi(d);
     }
-    hadamard32<H>(a);
-    hadamard32<H>(b);
+    butterfly32<H>(a);
+    butterfly32<H>(b);
     uint4 na, nb;
     uint32_t sa, sb;
-    encode_block<MODE>(a, na, sa);
-    encode_block<MODE>(b, nb, sb);
+    encode_block_sh<MODE, kScaleShift<H>>(a, na, sa);
+    encode_block_sh<MODE, kScaleShift<H>>(b, nb, sb);
     const int64_t ca = c0 + 2 * pr, cb = ca + 1;
     *reinterpret_cast<uint4*>(nib + ca * nib_pitch + band * 16) = na;
     *reinterpret_cast<uint4*>(nib + cb * nib_pitch + band * 16) = nb;
@@ -261,10 +263,10 @@ __global__ __launch_bounds__(64 * NB) void quant_col_staged_kernel(const uint16_
         const uint32_t d = j < 2 ? raw[r].x : raw[r].y;
         a[r] = (j & 1) ? bf16hi(d) : bf16lo(d);
       }
-      hadamard32<H>(a);
+      butterfly32<H>(a);
       uint4 na;
       uint32_t sa;
-      encode_block<MODE>(a, na, sa);
+      encode_block_sh<MODE, kScaleShift<H>>(a, na, sa);
       const int ca = lane * 4 + j;
       *reinterpret_cast<uint4*>(onib + (ca * NB + wave) * 16) = na;
       osc[ca * NB + wave] = (uint8_t)sa;
@@ -307,10 +309,10 @@ __global__ __launch_bounds__(256) void quant_col_scalar_kernel(const uint16_t* _
   float v[32];
 #pragma unroll
   for (int r = 0; r < 32; ++r) v[r] = __uint_as_float((uint32_t)src[(band * 32 + r) * cols + c] << 16);
-  hadamard32<H>(v);
+  butterfly32<H>(v);
   uint4 out;
   uint32_t s;
-  encode_block<MODE>(v, out, s);
+  encode_block_sh<MODE, kScaleShift<H>>(v, out, s);
   *reinterpret_cast<uint4*>(nib + c * (rows / 2) + band * 16) = out;
   sc[c * (rows / 32) + band] = (uint8_t)s;
 }
@@ -322,19 +324,24 @@ __global__ __launch_bounds__(256) void quant_col_scalar_kernel(const uint16_t* _
 // both from the same tensor. This kernel reads the bf16 tile once and emits
 // both packed operands, each exactly as mxfp4_quantize would.
 //
-// Tiling as the staged column path (NB = 8 or 4 bands of 32 rows; here also
-// cols % 256 == 0): lane l of wave w holds columns [c0, c0 + 4) of band
-// NB*rowgroup + w in registers. Column direction: unchanged. Row direction,
-// for each of the band's 32 rows: the lane's 4 values are columns 4l + j of
-// a 32-column block spread over 8 lanes; butterfly stages 1 and 2 pair
-// values inside the lane, stages 4, 8 (and 16 for H32) pair lanes l ^ 1,
-// l ^ 2 (and l ^ 4) through DPP quad permutations (and ds_swizzle), where
-// the lane holding the lower column forms a + b and its partner a - b, the
-// same operations in the same order as the in-register butterfly. The block
-// amax is reduced over the 8 lanes; each lane encodes its 4 values into 2
-// nibble bytes. Both outputs are staged in LDS and written with 16-byte
-// nibble stores (whole 128-byte lines per row and, with NB = 8, per column)
-// and 8- or 4-byte scale stores.
+// Tiling as the staged column path (4 bands of 32 rows; here also
+// cols % 256 == 0): lane l of wave w holds columns [4l, 4l + 4) of its
+// 256-column group for the 32 rows of band 4*rowgroup + w. Column
+// direction: unchanged. Row direction, per group of 4 rows: a 4x4 transpose
+// inside each quad of lanes (DPP quad permutations) gives lane 4q + p the 16
+// consecutive columns [16q, 16q + 16) of row 4g + p, so the H16 butterfly
+// runs in registers; the two 16-column halves of a 32-block sit in lanes l
+// and l ^ 4, which exchange once for the block amax (and, for H32, for the
+// butterfly's last stage). The kernel is VALU-bound (two rotations and two
+// encodes per element loaded), so the H16 1/4 moves into the scale
+// (kScaleShift) and the amax uses amax_bits_n. Both outputs are staged in
+// LDS and written with 16-byte nibble stores (whole 128-byte lines per row)
+// and 4- or 8-byte scale stores. Measured against the previous layout, in
+// which each row's 32-block stayed spread over 8 lanes (two cross-lane
+// butterfly stages and three cross-lane amax steps per row, 144 VGPRs, 3
+// waves per SIMD): 8192 x 4096 32.2 -> 23.7 us, 8192 x 14336 88.0 -> 75.1
+// us, bit-identical outputs.
+//
 // Lane exchange inside groups of 8 lanes: partner lane l ^ M. M = 1, 2 use a
 // DPP quad permutation (lane i of a quad reads lane sel[i]); M = 4 uses
 // ds_swizzle in bit mode (lane i reads lane ((i & 0x1f) | 0) ^ 4).
@@ -353,34 +360,27 @@ __device__ __forceinline__ float xchgf(float v) {
   return __uint_as_float(xchg<M>(__float_as_uint(v)));
 }
 
-// One cross-lane butterfly stage: the lane holding the lower column forms
-// own + partner (= a + b), its partner partner + (-own) (= a - b, the same
-// fp32 operation), with the sign flip applied to the lane's own value.
-template <int M>
-__device__ __forceinline__ void row_stage(float (&x)[4], int lane) {
-  const uint32_t flip = (lane & M) ? 0x80000000u : 0u;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float y = xchgf<M>(x[j]);
-    x[j] = y + __uint_as_float(__float_as_uint(x[j]) ^ flip);
-  }
+// Quad transpose with every partner value fetched unconditionally and then
+// selected (x[j] of lane p becomes x[p] of lane j). Same result as
+// quad_transpose; selecting what to send first, as there, lets the compiler
+// turn the DPP moves into branches around single lanes, which costs more
+// here where the transpose runs 16 times per wave.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_quad(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, true);
 }
 
-template <int H>
-__device__ __forceinline__ void row_butterfly4(float (&x)[4], int lane) {
-  if constexpr (H != 0) {
-    float a;
-    a = x[0]; x[0] = a + x[1]; x[1] = a - x[1];
-    a = x[2]; x[2] = a + x[3]; x[3] = a - x[3];
-    a = x[0]; x[0] = a + x[2]; x[2] = a - x[2];
-    a = x[1]; x[1] = a + x[3]; x[3] = a - x[3];
-    row_stage<1>(x, lane);
-    row_stage<2>(x, lane);
-    if constexpr (H == 32) row_stage<4>(x, lane);
-    const float c = (H == 16) ? 0.25f : __uint_as_float(0x3E3504F3u);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] *= c;
-  }
+__device__ __forceinline__ void quad_transpose_sel(uint32_t (&x)[4], bool b1, bool b0) {
+  const uint32_t d0 = dpp_quad<0x4e>(x[0]), d1 = dpp_quad<0x4e>(x[1]);
+  const uint32_t d2 = dpp_quad<0x4e>(x[2]), d3 = dpp_quad<0x4e>(x[3]);
+  const uint32_t y0 = b1 ? d2 : x[0], y1 = b1 ? d3 : x[1];
+  const uint32_t y2 = b1 ? x[2] : d0, y3 = b1 ? x[3] : d1;
+  const uint32_t e0 = dpp_quad<0xb1>(y0), e1 = dpp_quad<0xb1>(y1);
+  const uint32_t e2 = dpp_quad<0xb1>(y2), e3 = dpp_quad<0xb1>(y3);
+  x[0] = b0 ? e1 : y0;
+  x[1] = b0 ? y1 : e0;
+  x[2] = b0 ? e3 : y2;
+  x[3] = b0 ? y3 : e2;
 }
 
 template <int H, int MODE, int NB>
@@ -390,6 +390,7 @@ __global__ __launch_bounds__(64 * NB) void quant_dual_kernel(const uint16_t* __r
                                                              uint8_t* __restrict__ rsc,
                                                              uint8_t* __restrict__ cnib,
                                                              uint8_t* __restrict__ csc) {
+  constexpr int SH = kScaleShift<H>;
   __shared__ __attribute__((aligned(16))) uint8_t onib[256 * NB * 16];  // column output
   __shared__ __attribute__((aligned(16))) uint8_t osc[256 * NB];
   __shared__ __attribute__((aligned(16))) uint8_t lrn[32 * NB * 128];   // row output
@@ -405,26 +406,69 @@ __global__ __launch_bounds__(64 * NB) void quant_dual_kernel(const uint16_t* __r
 #pragma unroll
   for (int r = 0; r < 32; ++r) raw[r] = ld_nt8(p + r * cols);
   // row direction
+  const int q = lane >> 2, pq = lane & 3;
+  const bool b1 = (pq & 2) != 0, b0 = (pq & 1) != 0;
 #pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    float x[4] = {bf16lo(raw[r].x), bf16hi(raw[r].x), bf16lo(raw[r].y), bf16hi(raw[r].y)};
-    row_butterfly4<H>(x, lane);
-    uint32_t am = 0;
+  for (int g = 0; g < 8; ++g) {
+    uint32_t xs[4], ys[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) am = max(am, __float_as_uint(x[j]) & 0x7fffffffu);
-    am = max(am, xchg<1>(am));
-    am = max(am, xchg<2>(am));
-    am = max(am, xchg<4>(am));
-    const uint32_t s = e8m0_byte<MODE>(am);
-    uint32_t w = 0;
-    if (s != 255u) {
-      const float scale = scale_of_byte(s);
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[0], x[1], scale, 0);
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2], x[3], scale, 1);
+    for (int i = 0; i < 4; ++i) {
+      xs[i] = raw[4 * g + i].x;
+      ys[i] = raw[4 * g + i].y;
     }
-    const int lr = wave * 32 + r;
-    *reinterpret_cast<uint16_t*>(lrn + lr * 128 + lane * 2) = (uint16_t)w;
-    if ((lane & 7) == 0) lrs[lr * 8 + (lane >> 3)] = (uint8_t)s;
+    quad_transpose_sel(xs, b1, b0);
+    quad_transpose_sel(ys, b1, b0);
+    float v[16];  // columns 16q + k of row 4g + pq
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[4 * i] = bf16lo(xs[i]);
+      v[4 * i + 1] = bf16hi(xs[i]);
+      v[4 * i + 2] = bf16lo(ys[i]);
+      v[4 * i + 3] = bf16hi(ys[i]);
+    }
+    if constexpr (H != 0) {
+#pragma unroll
+      for (int s = 1; s < 16; s <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if ((i & s) == 0) {
+            const float a = v[i], b = v[i + s];
+            v[i] = a + b;
+            v[i + s] = a - b;
+          }
+        }
+      }
+    }
+    if constexpr (H == 32) {
+      // stage 16: the lane with the lower half forms own + partner (a + b),
+      // its partner partner + (-own) (a - b, the same fp32 operation)
+      const uint32_t flip = (lane & 4) ? 0x80000000u : 0u;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float y = xchgf<4>(v[i]);
+        v[i] = y + __uint_as_float(__float_as_uint(v[i]) ^ flip);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] *= __uint_as_float(0x3E3504F3u);
+    }
+    uint32_t am = amax_bits_n<16>(v);
+    am = max(am, xchg<4>(am));
+    const uint32_t s = e8m0_byte_sh<MODE, SH>(am);
+    uint32_t w0 = 0, w1 = 0;
+    if (s != 255u) {
+      const float scale = cvt_scale<SH>(s);
+      w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[0], v[1], scale, 0);
+      w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[2], v[3], scale, 1);
+      w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[4], v[5], scale, 2);
+      w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, v[6], v[7], scale, 3);
+      w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[8], v[9], scale, 0);
+      w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[10], v[11], scale, 1);
+      w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[12], v[13], scale, 2);
+      w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, v[14], v[15], scale, 3);
+    }
+    const int lr = wave * 32 + 4 * g + pq;
+    *reinterpret_cast<uint2*>(lrn + lr * 128 + 8 * q) = make_uint2(w0, w1);
+    if ((q & 1) == 0) lrs[lr * 8 + (q >> 1)] = (uint8_t)s;
   }
   // column direction
 #pragma unroll
@@ -435,10 +479,10 @@ __global__ __launch_bounds__(64 * NB) void quant_dual_kernel(const uint16_t* __r
       const uint32_t d = j < 2 ? raw[r].x : raw[r].y;
       a[r] = (j & 1) ? bf16hi(d) : bf16lo(d);
     }
-    hadamard32<H>(a);
+    butterfly32<H>(a);
     uint4 na;
     uint32_t sa;
-    encode_block<MODE>(a, na, sa);
+    encode_block_sh<MODE, SH>(a, na, sa);
     const int ca = lane * 4 + j;
     *reinterpret_cast<uint4*>(onib + (ca * NB + wave) * 16) = na;
     osc[ca * NB + wave] = (uint8_t)sa;
@@ -449,13 +493,13 @@ __global__ __launch_bounds__(64 * NB) void quant_dual_kernel(const uint16_t* __r
   const int64_t rpitch = cols / 2, rspitch = cols / 32;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int q = t + 64 * NB * i;
-    // column output: 16-byte chunk q = (column q / NB, band q % NB)
-    *reinterpret_cast<uint4*>(cnib + (cg * 256 + q / NB) * npitch + rg * 16 * NB + (q % NB) * 16) =
-        *reinterpret_cast<const uint4*>(onib + q * 16);
-    // row output: 16-byte chunk q = (row q / 8, chunk q % 8)
-    *reinterpret_cast<uint4*>(rnib + (rg * 32 * NB + (q >> 3)) * rpitch + cg * 128 + (q & 7) * 16) =
-        *reinterpret_cast<const uint4*>(lrn + q * 16);
+    const int k = t + 64 * NB * i;
+    // column output: 16-byte chunk k = (column k / NB, band k % NB)
+    *reinterpret_cast<uint4*>(cnib + (cg * 256 + k / NB) * npitch + rg * 16 * NB + (k % NB) * 16) =
+        *reinterpret_cast<const uint4*>(onib + k * 16);
+    // row output: 16-byte chunk k = (row k / 8, chunk k % 8)
+    *reinterpret_cast<uint4*>(rnib + (rg * 32 * NB + (k >> 3)) * rpitch + cg * 128 + (k & 7) * 16) =
+        *reinterpret_cast<const uint4*>(lrn + k * 16);
   }
   if (t < 256) {
     if constexpr (NB == 8)
