@@ -711,6 +711,98 @@ __global__ __launch_bounds__(256) void quant_mbs_col_kernel(const uint16_t* __re
   mbs[c * (rows / 128) + mb] = (uint8_t)m;
 }
 
+// Column axis, staged (rows % 128 == 0, cols % 4 == 0, nibble and scale
+// pointers 16- and 4-byte aligned): a work-group of 4 waves covers one
+// 128-row macro band x 256 columns, the column quantizer's tile with 4
+// bands. Lane l of wave w loads its 4 columns of band w (32 rows, 8-byte
+// non-temporal loads), rotates them and keeps the 128 rotated values in
+// registers; the block amaxes meet in LDS, where each lane takes the
+// macro-block maximum of its columns over the 4 waves. The prescale needs
+// no second pass over the values' maxima: fl32 rounding is monotonic, so the
+// amax of fl32(c y) is fl32(c amax(y)). For H16 the values stay
+// unnormalised (u = 4 y, exact) and the 1/4 joins the prescale:
+// fl32((c / 4) u) is the same single rounding of c y. Outputs are staged in
+// LDS and leave as 64-byte nibble runs and 4-byte scale words per column.
+template <int H, int MODE>
+__global__ __launch_bounds__(256) void quant_mbs_col_staged_kernel(
+    const uint16_t* __restrict__ src, int64_t rows, int64_t cols, uint8_t* __restrict__ nib,
+    uint8_t* __restrict__ sc, uint8_t* __restrict__ mbs) {
+  constexpr int NB = 4;
+  __shared__ __attribute__((aligned(16))) uint8_t onib[256 * NB * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t osc[256 * NB];
+  __shared__ __attribute__((aligned(16))) uint32_t lam[NB][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t ncg = (cols + 255) / 256;
+  const int64_t cg = (int64_t)blockIdx.x % ncg;
+  const int64_t mb = (int64_t)blockIdx.x / ncg;
+  const int64_t c0 = cg * 256 + (int64_t)lane * 4;
+  const bool live = c0 < cols;
+  float u[4][32];
+  uint32_t bam[4] = {0u, 0u, 0u, 0u};
+  if (live) {
+    const uint16_t* p = src + (mb * NB + wave) * 32 * cols + c0;
+    uint2 raw[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) raw[r] = ld_nt8(p + r * cols);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        const uint32_t d = j < 2 ? raw[r].x : raw[r].y;
+        u[j][r] = (j & 1) ? bf16hi(d) : bf16lo(d);
+      }
+      butterfly32<H>(u[j]);
+      bam[j] = amax_bits_n<32>(u[j]);
+    }
+  }
+  *reinterpret_cast<uint4*>(&lam[wave][lane * 4]) = make_uint4(bam[0], bam[1], bam[2], bam[3]);
+  __syncthreads();
+  if (live) {
+    uint32_t mcol[4];
+    {
+      const uint4 a0 = *reinterpret_cast<const uint4*>(&lam[0][lane * 4]);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(&lam[1][lane * 4]);
+      const uint4 a2 = *reinterpret_cast<const uint4*>(&lam[2][lane * 4]);
+      const uint4 a3 = *reinterpret_cast<const uint4*>(&lam[3][lane * 4]);
+      mcol[0] = max(max(a0.x, a1.x), max(a2.x, a3.x));
+      mcol[1] = max(max(a0.y, a1.y), max(a2.y, a3.y));
+      mcol[2] = max(max(a0.z, a1.z), max(a2.z, a3.z));
+      mcol[3] = max(max(a0.w, a1.w), max(a2.w, a3.w));
+    }
+    const int64_t mpitch = rows / 128;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // macro amax of the rotated values (H16: u / 4, exact in fp32)
+      const uint32_t M = (H == 16) ? __float_as_uint(__uint_as_float(mcol[j]) * 0.25f) : mcol[j];
+      const uint32_t m = mbs_byte(M);
+      const float cf = 1.0f + (float)m * 0.00390625f;
+      const float ck = (H == 16) ? cf * 0.25f : cf;
+#pragma unroll
+      for (int r = 0; r < 32; ++r) u[j][r] = ck * u[j][r];
+      const uint32_t s = e8m0_byte<MODE>(__float_as_uint(ck * __uint_as_float(bam[j])));
+      const uint4 na = (s == 255u) ? make_uint4(0, 0, 0, 0) : encode32(u[j], scale_of_byte(s));
+      const int ca = lane * 4 + j;
+      *reinterpret_cast<uint4*>(onib + (ca * NB + wave) * 16) = na;
+      osc[ca * NB + wave] = (uint8_t)s;
+      if (wave == 0) mbs[(c0 + j) * mpitch + mb] = (uint8_t)m;
+    }
+  }
+  __syncthreads();
+  const int64_t npitch = rows / 2, spitch = rows / 32;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = threadIdx.x + 64 * NB * i;  // 16-byte chunk: column k / NB, band k % NB
+    const int64_t col = cg * 256 + k / NB;
+    if (col < cols)
+      *reinterpret_cast<uint4*>(nib + col * npitch + mb * 16 * NB + (k % NB) * 16) =
+          *reinterpret_cast<const uint4*>(onib + k * 16);
+  }
+  const int64_t col = cg * 256 + threadIdx.x;
+  if (col < cols)
+    *reinterpret_cast<uint32_t*>(sc + col * spitch + mb * 4) =
+        *reinterpret_cast<const uint32_t*>(osc + threadIdx.x * 4);
+}
+
 template <int H, int MODE>
 hipError_t dispatch_mbs(const void* src, int64_t rows, int64_t cols, int axis, void* nib,
                         void* sc, void* mbs, hipStream_t st) {
@@ -719,6 +811,12 @@ hipError_t dispatch_mbs(const void* src, int64_t rows, int64_t cols, int axis, v
     hipLaunchKernelGGL((quant_mbs_row_kernel<H, MODE>), dim3((unsigned)((nblocks + 255) / 256)),
                        dim3(256), 0, st, static_cast<const uint4*>(src), nblocks,
                        static_cast<uint4*>(nib), static_cast<uint8_t*>(sc),
+                       static_cast<uint8_t*>(mbs));
+  } else if (cols % 4 == 0 && (uintptr_t)nib % 16 == 0 && (uintptr_t)sc % 4 == 0) {
+    const int64_t grid = (rows / 128) * ((cols + 255) / 256);
+    hipLaunchKernelGGL((quant_mbs_col_staged_kernel<H, MODE>), dim3((unsigned)grid), dim3(256), 0,
+                       st, static_cast<const uint16_t*>(src), rows, cols,
+                       static_cast<uint8_t*>(nib), static_cast<uint8_t*>(sc),
                        static_cast<uint8_t*>(mbs));
   } else {
     const int64_t grid = (rows / 128) * ((cols + 255) / 256);

@@ -40,8 +40,12 @@ def test_small_shapes_bit_exact(axis, h, mode):
 @pytest.mark.parametrize("axis", [0, 1])
 @pytest.mark.parametrize("mode", [0, 1])
 def test_edge_values_bit_exact(axis, mode):
-    for h in (0, 16, 32):
-        assert_mbs_same(edge_matrix(128, 256, seed=23), axis, h, mode, f"edge axis={axis} h={h}")
+    mats = [edge_matrix(128, 256, seed=23)]
+    if axis == 1:  # special blocks down the columns as well
+        mats.append(np.ascontiguousarray(edge_matrix(256, 128, seed=24).T))
+    for k, bits in enumerate(mats):
+        for h in (0, 16, 32):
+            assert_mbs_same(bits, axis, h, mode, f"edge {k} axis={axis} h={h}")
 
 
 @pytest.mark.parametrize("axis", [0, 1])
