@@ -518,35 +518,48 @@ __global__ __launch_bounds__(64 * NB) void quant_dual_kernel(const uint16_t* __r
 // [P3] "three targeted fixes" section, OF: x_OF = Q(x) + alpha Q(x - Q(x)),
 // alpha = 1/2, here applied as a prescale of the residual, Q(r / 2) (equal to
 // Q(r) / 2 unless the residual block sits at the E8M0 floor). Per 32-block:
-// quantize, decode the codes back to fp32 (exact: an E2M1 value times
-// 2^E), r = y - q1 and h = r / 2 in fp32 (one rounding each), quantize h.
+// quantize, decode the codes back to fp32 (an E2M1 value times 2^E, exact
+// unless it overflows), r = y - q1 and h = r / 2 in fp32 (one rounding
+// each), quantize h. The values stay normalised here (no folded H16 scale):
+// near the fp32 maximum the decode of 4 q1 can overflow where that of q1
+// does not.
 // The output is one K-concatenated operand: row i = q1's row, then q2's
 // row; a GEMM of depth 2 Kb against the other operand repeated along K
 // computes sum (q1 + q2) b. A non-finite block is 0xFF in both halves.
-__device__ __forceinline__ float e2m1_value(uint32_t code) {
-  const uint32_t m = code & 7u;
-  const float v = m < 4u ? 0.5f * (float)m : (m == 4u ? 2.f : (m == 5u ? 3.f : (m == 6u ? 4.f : 6.f)));
-  return (code & 8u) ? -v : v;
-}
+// The first pass is decoded with gfx950's scaled FP4-to-fp32 convert, which
+// returns the E2M1 value times the fp32 scale as one IEEE multiply (an
+// in-bounds probe over all 16 codes and all 255 scale bytes matched fp32
+// products bit for bit, subnormal results and overflow to +-Inf included).
+typedef float of_f32x2 __attribute__((ext_vector_type(2)));
 
 template <int MODE>
 __device__ __forceinline__ void of_block(float (&v)[32], uint4& n1, uint32_t& s1, uint4& n2,
                                          uint32_t& s2) {
-  encode_block<MODE>(v, n1, s1);
+  s1 = e8m0_byte<MODE>(amax_bits_n<32>(v));
   if (s1 == 255u) {
+    n1 = make_uint4(0, 0, 0, 0);
     n2 = make_uint4(0, 0, 0, 0);
     s2 = 255u;
     return;
   }
   const float sc = scale_of_byte(s1);
+  n1 = encode32(v, sc);
   const uint32_t w[4] = {n1.x, n1.y, n1.z, n1.w};
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float q = e2m1_value((w[i >> 3] >> (4 * (i & 7))) & 0xfu) * sc;
-    const float r = v[i] - q;
-    v[i] = 0.5f * r;
+  for (int d = 0; d < 4; ++d) {
+    of_f32x2 q[4];
+    q[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], sc, 0);
+    q[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], sc, 1);
+    q[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], sc, 2);
+    q[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], sc, 3);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[8 * d + 2 * k] = 0.5f * (v[8 * d + 2 * k] - q[k].x);
+      v[8 * d + 2 * k + 1] = 0.5f * (v[8 * d + 2 * k + 1] - q[k].y);
+    }
   }
-  encode_block<MODE>(v, n2, s2);
+  s2 = e8m0_byte<MODE>(amax_bits_n<32>(v));
+  n2 = (s2 == 255u) ? make_uint4(0, 0, 0, 0) : encode32(v, scale_of_byte(s2));
 }
 
 // Row axis: one thread per 32-block (block b of row b / ncb).
