@@ -34,51 +34,78 @@ namespace {
 constexpr int kStats = 10;
 constexpr int kThreads = 256;
 
+// Nearest E2M1 grid value of t (ties to the even code, clamp at 6) as a
+// chain of selects on |t|; the grid values differ only in their upper
+// dword, so each select is one 32-bit move. The sign is t's.
 __device__ __forceinline__ double grid_of(double t) {
   const double a = fabs(t);
-  int mag = (a > 0.25) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) + (a > 2.5) + (a >= 3.5) + (a > 5.0);
-  const double g = mag < 4 ? 0.5 * mag : (mag == 4 ? 2.0 : (mag == 5 ? 3.0 : (mag == 6 ? 4.0 : 6.0)));
-  return signbit(t) ? -g : g;
+  double g = 0.0;
+  g = a > 0.25 ? 0.5 : g;
+  g = a >= 0.75 ? 1.0 : g;
+  g = a > 1.25 ? 1.5 : g;
+  g = a >= 1.75 ? 2.0 : g;
+  g = a > 2.5 ? 3.0 : g;
+  g = a >= 3.5 ? 4.0 : g;
+  g = a > 5.0 ? 6.0 : g;
+  return copysign(g, t);
 }
 
-__device__ __forceinline__ double code_value(uint32_t code) {
-  const uint32_t m = code & 7u;
-  const double g = m < 4 ? 0.5 * m : (m == 4 ? 2.0 : (m == 5 ? 3.0 : (m == 6 ? 4.0 : 6.0)));
-  return (code & 8u) ? -g : g;
-}
+typedef float st_f32x2 __attribute__((ext_vector_type(2)));
 
+// Per element, in fp64: Q from the code (the scaled FP4-to-fp32 convert at
+// scale 1 gives the E2M1 value exactly; times 2^E in fp64), t = x / s*
+// (one correctly rounded division, as the oracle's), Q* = s* grid(t), the
+// deadzone test and the terms; each sum takes one fused multiply-add per
+// element. Every branch depends only on the block (non-finite, s* = 0), so
+// the per-element work is straight-line code.
 template <int MODE>
 __device__ __forceinline__ void block_stats(const float (&v)[32], double (&acc)[kStats]) {
-  const uint32_t am = amax_bits32(v);
+  const uint32_t am = amax_bits_n<32>(v);
   if (am >= 0x7f800000u) {
     acc[9] += 1.0;
     return;
   }
   const uint32_t sb = e8m0_byte<MODE>(am);
   const uint4 nib = encode32(v, scale_of_byte(sb));
-  const double p2 = ldexp(1.0, (int)sb - 127);
+  // 2^(sb - 127) as fp64 (sb - 127 >= -127 is a normal fp64 exponent)
+  const double p2 = __longlong_as_double((long long)((int64_t)(sb + 896u) << 52));
   const double mb = (double)__uint_as_float(am);
   const double ss = mb / 6.0;
+  // s* = 0 only for an all-zero block, whose t is 0 (x / 1)
+  const double sd = ss > 0.0 ? ss : 1.0;
   const uint32_t w[4] = {nib.x, nib.y, nib.z, nib.w};
+  double nd = 0.0;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const uint32_t code = (w[i >> 3] >> (4 * (i & 7))) & 0xfu;
-    const double x = (double)v[i];
-    const double q = code_value(code) * p2;
-    const double t = ss > 0.0 ? x / ss : 0.0;
-    const double qs = ss * grid_of(t);
-    const bool dz = 24.0 * fabs(x) < mb;
-    const double es = q - qs, r = qs - x, e = q - x;
-    const double edz = dz ? r : 0.0, eg = dz ? 0.0 : r;
-    acc[0] += es * es;
-    acc[1] += edz * edz;
-    acc[2] += eg * eg;
-    acc[3] += es * eg;
-    acc[4] += es * edz;
-    acc[5] += e * e;
-    acc[6] += x * x;
-    acc[7] += dz ? 1.0 : 0.0;
+  for (int d = 0; d < 4; ++d) {
+    st_f32x2 cvs[4];
+    cvs[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 0);
+    cvs[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 1);
+    cvs[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 2);
+    cvs[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 3);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const st_f32x2 cv = cvs[k];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int i = 8 * d + 2 * k + h;
+        const double x = (double)v[i];
+        const double q = (double)(h ? cv.y : cv.x) * p2;
+        const double qs = ss * grid_of(x / sd);
+        const bool dz = 24.0 * fabs(x) < mb;
+        const double es = q - qs, r = qs - x, e = q - x;
+        const double edz = dz ? r : 0.0, eg = dz ? 0.0 : r;
+        acc[0] = fma(es, es, acc[0]);
+        acc[1] = fma(edz, edz, acc[1]);
+        acc[2] = fma(eg, eg, acc[2]);
+        acc[3] = fma(es, eg, acc[3]);
+        acc[4] = fma(es, edz, acc[4]);
+        acc[5] = fma(e, e, acc[5]);
+        acc[6] = fma(x, x, acc[6]);
+        nd += dz ? 1.0 : 0.0;
+      }
+    }
   }
+  acc[7] += nd;
   acc[8] += 32.0;
 }
 
