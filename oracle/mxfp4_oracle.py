@@ -225,6 +225,93 @@ def quantize_chunked(src_bf16: np.ndarray, axis: int, hadamard: int, mode: int,
 
 
 # --------------------------------------------------------------------------
+# Error-only comparison arms that [P1] reports as diverging under full MXFP4
+# training (quick-read block and discussion: random Hadamard transforms and
+# stochastic rounding). They are built here to measure their quantization
+# error next to the deterministic H16 + round-to-nearest path; the random
+# numbers are inputs.
+# --------------------------------------------------------------------------
+def quantize_rs(src_bf16: np.ndarray, axis: int, hadamard: int, mode: int,
+                signs: np.ndarray):
+    """Random-sign Hadamard: rotate diag(s) x instead of x, s_i = -1 where
+    ``signs[i]`` is 1 and +1 where it is 0, i indexing the blocked
+    (reduction) axis: ``signs`` has ``cols`` entries for row blocks and
+    ``rows`` for column blocks. Both operands of a product take the same
+    signs, so (X D H)(W D H)^T = X W^T. A sign flip of a bf16 value is
+    exact, so this is ``quantize`` of the sign-flipped matrix."""
+    bits = np.asarray(src_bf16, dtype=np.uint16)
+    s = np.asarray(signs, dtype=np.uint8)
+    if axis == AXIS_ROW:
+        if s.shape != (bits.shape[1],):
+            raise ValueError("row blocks take one sign per column")
+        flip = s[None, :]
+    elif axis == AXIS_COL:
+        if s.shape != (bits.shape[0],):
+            raise ValueError("column blocks take one sign per row")
+        flip = s[:, None]
+    else:
+        raise ValueError("random signs are defined here for 1x32 and 32x1 blocks")
+    if np.any(s > 1):
+        raise ValueError("signs are 0 or 1")
+    return quantize(bits ^ (flip.astype(np.uint16) << np.uint16(15)), axis, hadamard, mode)
+
+
+def sr_codes(y: np.ndarray, E: np.ndarray, rnd: np.ndarray) -> np.ndarray:
+    """Stochastic-rounding codes (sign << 3 | magnitude) of y / 2^E.
+
+    a = |y| 2^-E (exact in fp64). Below 6, with g_lo <= a < g_hi the two
+    neighbouring grid values, p = (a - g_lo) / (g_hi - g_lo) (exact: the
+    gap is 0.5, 1 or 2) and the magnitude rounds up to g_hi exactly when
+    rnd < p 2^32, i.e. with probability p for a uniform 32-bit rnd, so
+    that the expected value is a. a >= 6 saturates to 6. The sign bit of
+    y is kept, as in ``e2m1_code``.
+    """
+    y = np.asarray(y, dtype=np.float32)
+    a = np.abs(np.ldexp(y.astype(np.float64), -np.asarray(E, dtype=np.int64)))
+    lo = ((a >= 0.5).astype(np.int64) + (a >= 1.0) + (a >= 1.5) + (a >= 2.0) + (a >= 3.0)
+          + (a >= 4.0) + (a >= 6.0))
+    g_lo = E2M1_GRID[lo]
+    gap = E2M1_GRID[np.minimum(lo + 1, 7)] - g_lo
+    with np.errstate(invalid="ignore", divide="ignore"):
+        p = np.where(lo < 7, (a - g_lo) / np.where(gap > 0, gap, 1.0), 0.0)
+    up = np.asarray(rnd, dtype=np.uint32).astype(np.float64) < p * 4294967296.0
+    mag = np.where(lo >= 7, 7, lo + up).astype(np.uint8)
+    sign = np.signbit(y).astype(np.uint8)
+    return (sign << 3) | mag
+
+
+def quantize_sr(src_bf16: np.ndarray, axis: int, hadamard: int, mode: int,
+                rand_u32: np.ndarray):
+    """Stochastic-rounding operand: the scales of ``quantize`` (same E8M0
+    rule on the same block maxima), element codes from ``sr_codes`` with
+    one uniform 32-bit integer per source element (``rand_u32`` has the
+    source's shape [rows][cols]; element (r, c) uses rand_u32[r][c] for
+    either axis). Non-finite blocks are 0xFF with zero nibbles."""
+    x = bf16_to_f32(src_bf16)
+    rnd = np.asarray(rand_u32, dtype=np.uint32)
+    if rnd.shape != x.shape:
+        raise ValueError("one random integer per source element")
+    if axis == AXIS_COL:
+        x = np.ascontiguousarray(x.T)
+        rnd = np.ascontiguousarray(rnd.T)
+    elif axis != AXIS_ROW:
+        raise ValueError("stochastic rounding is defined here for 1x32 and 32x1 blocks")
+    if x.shape[1] % BLOCK:
+        raise ValueError("blocked axis must be a multiple of 32")
+    y = hadamard_rotate(x, hadamard)
+    r, c = y.shape
+    yb = y.reshape(r, c // BLOCK, BLOCK)
+    m_b = np.max(np.abs(yb), axis=2)
+    finite = np.all(np.isfinite(yb), axis=2)
+    m_b = np.where(finite, m_b, np.float32(0))
+    E = e8m0_exponent(m_b, mode)
+    codes = sr_codes(yb, E[:, :, None], rnd.reshape(r, c // BLOCK, BLOCK))
+    codes = np.where(finite[:, :, None], codes, np.uint8(0))
+    sc = np.where(finite, E + 127, 255).astype(np.uint8)
+    return _pack_nibbles(codes.reshape(r, c)), sc
+
+
+# --------------------------------------------------------------------------
 # Outlier fallback ([P3] "three targeted fixes" section, OF: two-step
 # residual quantization x_OF = Q(x) + alpha Q(x - Q(x)), alpha = 0.5)
 # --------------------------------------------------------------------------

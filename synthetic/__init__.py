@@ -38,7 +38,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["f64_to_bf16_bits", "bf16_bits_to_f32", "make", "WORKLOADS"]
+__all__ = ["f64_to_bf16_bits", "bf16_bits_to_f32", "make", "WORKLOADS", "random_signs",
+           "random_u32"]
 
 
 def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -134,3 +135,15 @@ WORKLOADS = {
     "mlp_down_dgrad": ("mlp", "dgrad", 8192, 4096, 14336),
     "down_wgrad": ("wgrad", "wgrad", 8192, 4096, 14336),
 }
+
+
+def random_signs(n: int, seed: int) -> np.ndarray:
+    """n sign flags (uint8 0 or 1, equally likely) for the random-sign
+    Hadamard comparison arm: ``default_rng(seed).integers(0, 2, n)``."""
+    return np.random.default_rng(seed).integers(0, 2, size=n, dtype=np.uint8)
+
+
+def random_u32(shape, seed: int) -> np.ndarray:
+    """Uniform 32-bit integers (uint32) for the stochastic-rounding arm:
+    ``default_rng(seed).integers(0, 2**32, shape)``."""
+    return np.random.default_rng(seed).integers(0, 2 ** 32, size=shape, dtype=np.uint32)

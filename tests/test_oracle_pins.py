@@ -701,3 +701,129 @@ def test_product_operand_orientation():
         if want is None:
             want = P @ Q.T
         assert np.array_equal(C, want), op
+
+
+# ------------------------------------------- comparison arms: random signs, SR
+def _codes_of(nib):
+    """Unpack [R][C/2] nibble bytes to [R][C] codes."""
+    c = np.empty((nib.shape[0], nib.shape[1] * 2), np.uint8)
+    c[:, 0::2] = nib & 0xF
+    c[:, 1::2] = nib >> 4
+    return c
+
+
+@pytest.mark.parametrize("axis", [O.AXIS_ROW, O.AXIS_COL])
+@pytest.mark.parametrize("h", [0, 16, 32])
+def test_random_signs_zero_and_all_flipped(axis, h):
+    """No flips is the plain operand; flipping every sign negates every
+    rotated value (the butterfly and the nearest-value rule are odd
+    functions), so only the nibbles' sign bits change."""
+    x = synthetic.f64_to_bf16_bits(np.random.default_rng(5).standard_t(3, size=(64, 96)))
+    n = x.shape[1] if axis == O.AXIS_ROW else x.shape[0]
+    for mode in (O.MODE_OCP_FLOOR, O.MODE_CEIL):
+        nib, sc = O.quantize(x, axis, h, mode)
+        z = O.quantize_rs(x, axis, h, mode, np.zeros(n, np.uint8))
+        f = O.quantize_rs(x, axis, h, mode, np.ones(n, np.uint8))
+        assert np.array_equal(z[0], nib) and np.array_equal(z[1], sc)
+        assert np.array_equal(f[0], nib ^ 0x88) and np.array_equal(f[1], sc)
+
+
+def test_random_signs_column_rule_is_row_rule_of_transpose():
+    x = synthetic.f64_to_bf16_bits(np.random.default_rng(6).standard_normal((96, 64)))
+    s = synthetic.random_signs(96, 7)
+    a = O.quantize_rs(x, O.AXIS_COL, 16, 1, s)
+    b = O.quantize_rs(np.ascontiguousarray(x.T), O.AXIS_ROW, 16, 1, s)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_random_signs_cancel_in_the_product():
+    """With the same signs on both operands along the reduction axis,
+    (X D H)(W D H)^T = X W^T: the quantized product stays within MXFP4's
+    error of the exact one (rel. Frobenius ~0.1), while signs drawn
+    independently for the two operands destroy it (~1.4)."""
+    rng = np.random.default_rng(8)
+    X = synthetic.f64_to_bf16_bits(rng.standard_normal((64, 256)))
+    W = synthetic.f64_to_bf16_bits(rng.standard_normal((48, 256)))
+    P = synthetic.bf16_bits_to_f32(X).astype(np.float64) @ synthetic.bf16_bits_to_f32(W).astype(np.float64).T
+    s = synthetic.random_signs(256, 9)
+    t = synthetic.random_signs(256, 10)
+    for h in (16, 32):
+        a = O.dequantize(*O.quantize_rs(X, O.AXIS_ROW, h, 1, s))
+        same = O.dequantize(*O.quantize_rs(W, O.AXIS_ROW, h, 1, s))
+        other = O.dequantize(*O.quantize_rs(W, O.AXIS_ROW, h, 1, t))
+        rel = lambda C: np.linalg.norm(C - P) / np.linalg.norm(P)
+        assert rel(a @ same.T) < 0.2
+        assert rel(a @ other.T) > 0.9
+
+
+def _grid_floor_ceil(v):
+    """Largest grid value <= |v| and smallest grid value >= |v| (capped at
+    6), by exact rational comparison."""
+    g = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
+         Fraction(4), Fraction(6)]
+    a = abs(Fraction(float(v)))
+    lo = max(i for i in range(8) if g[i] <= a)
+    hi = lo if (a == g[lo] or lo == 7) else lo + 1
+    return lo, hi
+
+
+@pytest.mark.parametrize("mode", [O.MODE_OCP_FLOOR, O.MODE_CEIL])
+def test_sr_extreme_random_values_floor_and_ceil(mode):
+    """rand = 2^32 - 1 never rounds up (p < 1 - 2^-32 for every fp32
+    input), so SR is the grid floor of |v|; rand = 0 rounds up whenever
+    p > 0, so SR is the grid ceiling (6 at most). Scales equal the
+    round-to-nearest operand's. No rotation, so v = x / 2^E with E from
+    the scale byte."""
+    rng = np.random.default_rng(11 + mode)
+    x = synthetic.f64_to_bf16_bits(rng.standard_t(3, size=(16, 64)))
+    nib_rtn, sc_rtn = O.quantize(x, O.AXIS_ROW, 0, mode)
+    xf = synthetic.bf16_bits_to_f32(x)
+    for r, which in ((np.uint32(0xFFFFFFFF), 0), (np.uint32(0), 1)):
+        nib, sc = O.quantize_sr(x, O.AXIS_ROW, 0, mode, np.full(x.shape, r, np.uint32))
+        assert np.array_equal(sc, sc_rtn)
+        codes = _codes_of(nib)
+        for i in range(16):
+            for j in range(64):
+                E = int(sc[i, j // 32]) - 127
+                lohi = _grid_floor_ceil(math.ldexp(float(xf[i, j]), -E))
+                want = lohi[which] | (8 if np.signbit(xf[i, j]) else 0)
+                assert codes[i, j] == want, (r, i, j)
+
+
+def test_sr_exact_threshold():
+    """A block with amax 4 has scale 2^0 in both rules; its value 0.375 lies
+    3/4 of the way from 0 to 0.5 and rounds up for rand < 0.75 * 2^32;
+    5.0 lies half way from 4 to 6 (threshold 2^31); 3.5 half way from 3
+    to 4."""
+    row = np.zeros(32)
+    row[0], row[1], row[2], row[3] = 4.0, 0.375, 5.0, -3.5
+    x = synthetic.f64_to_bf16_bits(row[None, :])
+    for mode in (O.MODE_OCP_FLOOR, O.MODE_CEIL):
+        for r1, c1 in ((3221225471, 1), (3221225472, 0)):
+            for r2, c2 in ((2 ** 31 - 1, 7), (2 ** 31, 6)):
+                rnd = np.full((1, 32), 0xFFFFFFFF, np.uint32)
+                rnd[0, 1], rnd[0, 2], rnd[0, 3] = r1, r2, r2
+                nib, sc = O.quantize_sr(x, O.AXIS_ROW, 0, mode, rnd)
+                assert sc[0, 0] == 127
+                codes = _codes_of(nib)[0]
+                assert codes[0] == 6 and codes[1] == c1 and codes[2] == c2
+                assert codes[3] == 8 | (6 if r2 < 2 ** 31 else 5)
+
+
+def test_sr_is_unbiased():
+    """Averaged over independent draws, the dequantized SR value is the
+    scaled input (the expected value of a stochastic rounding): each mean is
+    within 6 standard errors (gap / 2 / sqrt(n)) of x; a reversed
+    probability would miss by up to half a gap."""
+    rng = np.random.default_rng(13)
+    x = synthetic.f64_to_bf16_bits(rng.standard_normal((8, 64)))
+    xf = synthetic.bf16_bits_to_f32(x).astype(np.float64)
+    n = 400
+    acc = np.zeros(xf.shape)
+    for k in range(n):
+        nib, sc = O.quantize_sr(x, O.AXIS_ROW, 0, O.MODE_CEIL, synthetic.random_u32(x.shape, 100 + k))
+        acc += O.dequantize(nib, sc)
+    mean = acc / n
+    scale = np.repeat(np.ldexp(1.0, sc.astype(np.int64) - 127), 32, axis=1)
+    gap = np.where(np.abs(xf) / scale < 2, 0.5, np.where(np.abs(xf) / scale < 4, 1.0, 2.0)) * scale
+    assert np.all(np.abs(mean - xf) <= 6 * gap / 2 / math.sqrt(n))
