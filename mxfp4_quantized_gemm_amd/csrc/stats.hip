@@ -54,7 +54,7 @@ typedef float st_f32x2 __attribute__((ext_vector_type(2)));
 
 // Per element, in fp64: Q from the code (the scaled FP4-to-fp32 convert at
 // scale 1 gives the E2M1 value exactly; times 2^E in fp64), t = x / s*
-// (one correctly rounded division, as the oracle's), Q* = s* grid(t), the
+// (one correctly rounded fp64 division), Q* = s* grid(t), the
 // deadzone test and the terms; each sum takes one fused multiply-add per
 // element. Every branch depends only on the block (non-finite, s* = 0), so
 // the per-element work is straight-line code.
