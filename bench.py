@@ -134,6 +134,20 @@ def cpu_baseline(work, budget_rows=2048, budget_cols=8192):
                       f"dequantize, fp64 GEMM and sum|a||b| (numpy; BLAS threads = {cores})"}
 
 
+def gemm_error(mx, an, asc, bn, bsc, p, ref, rows, stream):
+    """Error statistics of mxfp4_gemm(A, B) (first `rows` output rows)
+    against the fp64 reference `ref`."""
+    import numpy as np
+    mx.mxfp4_gemm(an, asc, bn, bsc, p["GM"], p["GN"], p["GK"], p["C"], mx.OUT_F32, stream)
+    c = p["C"][:rows].double()
+    d = c - ref
+    nd, nr = float((d * d).sum()), float((ref * ref).sum())
+    return {"mse": float((d * d).mean()),
+            "cosine": float((c * ref).sum() / (c.norm() * ref.norm())),
+            "rel_fro": (nd / nr) ** 0.5,
+            "snr_db": 10.0 * np.log10(nr / nd)}
+
+
 def error_report(mx, torch, prods, stream, dev, rows=128):
     """Quantization error of each product's fused entry point against the
     exact product of its original bf16 operands (fp64 on the GPU, first
@@ -181,6 +195,24 @@ def error_report(mx, torch, prods, stream, dev, rows=128):
                     "rel_fro": (nd / nr) ** 0.5,
                     "snr_db": 10.0 * np.log10(nr / nd)}
                 del an, asc, bn, bsc, a2n, a2s
+            # comparison arms ([P1]: random Hadamard and stochastic rounding
+            # diverge in training): the same signs on both operands along K;
+            # independent random integers for the two operands
+            import synthetic
+            signs = torch.from_numpy(synthetic.random_signs(p["K"], 61)).to(dev)
+            for m in (0, 1):
+                an, asc = mx.quantize_rs(p["P"], signs, mx.AXIS_ROW, 16, m, stream)
+                bn, bsc = mx.quantize_rs(p["Q"], signs, mx.AXIS_ROW, 16, m, stream)
+                rec[f"rs_h16_{['ocp_floor', 'ceil'][m]}"] = gemm_error(
+                    mx, an, asc, bn, bsc, p, ref, rows, stream)
+                del an, asc, bn, bsc
+                ra = torch.from_numpy(synthetic.random_u32(tuple(p["P"].shape), 62).view(np.int32)).to(dev)
+                rb = torch.from_numpy(synthetic.random_u32(tuple(p["Q"].shape), 63).view(np.int32)).to(dev)
+                an, asc = mx.quantize_sr(p["P"], ra, mx.AXIS_ROW, 16, m, stream)
+                bn, bsc = mx.quantize_sr(p["Q"], rb, mx.AXIS_ROW, 16, m, stream)
+                rec[f"sr_h16_{['ocp_floor', 'ceil'][m]}"] = gemm_error(
+                    mx, an, asc, bn, bsc, p, ref, rows, stream)
+                del an, asc, bn, bsc, ra, rb
         out[p["name"]] = rec
         del ref
     torch.cuda.synchronize()
@@ -529,6 +561,38 @@ def main():
                 "us": round(mean_ms * 1e3, 2), "GB/s": round(b / (mean_ms * 1e-3) / 1e9, 1),
                 "frac_hbm": round(b / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
             del outs
+        # comparison arms: random-sign H16 (signs along the blocked axis) and
+        # stochastic rounding (one 32-bit random integer per element, read too)
+        for ax in (0, 1):
+            ns_, ss_ = mx.packed_shapes(R, Cc, ax)
+            outs = [(torch.empty(ns_, dtype=torch.uint8, device=dev),
+                     torch.empty(ss_, dtype=torch.uint8, device=dev)) for _ in range(nsets)]
+            signs = torch.from_numpy(synthetic.random_signs(Cc if ax == 0 else R, 51)).to(dev)
+            rnd = [torch.from_numpy(synthetic.random_u32((R, Cc), 52 + k).view(np.int32)).to(dev)
+                   for k in range(2)]
+            for arm in ("rs", "sr"):
+                def qa(i):
+                    k = i % nsets
+                    if arm == "rs":
+                        mx.mxfp4_quantize_rs(srcs[k], R, Cc, ax, 16, 0, signs, outs[k][0],
+                                             outs[k][1], stream)
+                    else:
+                        mx.mxfp4_quantize_sr(srcs[k], R, Cc, ax, 16, 0, rnd[i % 2], outs[k][0],
+                                             outs[k][1], stream)
+                for i in range(10):
+                    qa(i)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for i in range(its):
+                    qa(i)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                mean_ms = e0.elapsed_time(e1) / its
+                b = quant_bytes(R, Cc, ax) + (4 * R * Cc if arm == "sr" else 0)
+                quant[f"{arm}_{['row', 'col'][ax]}_h16_ocp_floor"] = {
+                    "us": round(mean_ms * 1e3, 2), "GB/s": round(b / (mean_ms * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(b / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            del outs, rnd, signs
         if "row_h16_ocp_floor" in quant and "row_h32_ocp_floor" in quant:
             quant["h16_over_h32_row"] = round(quant["row_h16_ocp_floor"]["GB/s"] /
                                               quant["row_h32_ocp_floor"]["GB/s"], 3)

@@ -168,6 +168,48 @@ int mxfp4_quantize_mbs(const void* src_bf16, int64_t rows, int64_t cols, int axi
                        void* out_mbs, hipStream_t stream);
 
 /*
+ * mxfp4_quantize_rs -- random-sign Hadamard comparison arm. [P1]'s
+ * quick-read block and discussion report that random Hadamard transforms
+ * (random sign flips before the rotation) diverge under full MXFP4
+ * training, where the deterministic H16 trains; this entry point produces
+ * such an operand so that its quantization error can be measured.
+ *
+ * Writes exactly what mxfp4_quantize (axis ROW or COL) writes for diag(s)
+ * src, s_i = -1 where bit 0 of signs[i] is set and +1 where it is clear,
+ * i indexing the blocked (rotated) axis. signs: DEVICE bytes, [cols] for
+ * MXFP4_AXIS_ROW (16-byte aligned) or [rows] for MXFP4_AXIS_COL, owned by
+ * the caller. The two operands of a product take the same signs along the
+ * reduction axis, so the signs cancel in the product. A NULL signs with a
+ * non-empty shape returns MXFP4_ERR_NULL, a misaligned one (row axis)
+ * MXFP4_ERR_ALIGN; otherwise errors as mxfp4_quantize (axis 2D32 returns
+ * MXFP4_ERR_MODE).
+ */
+int mxfp4_quantize_rs(const void* src_bf16, int64_t rows, int64_t cols, int axis,
+                      int hadamard, int scale_mode, const void* signs, void* out_nibbles,
+                      void* out_e8m0, hipStream_t stream);
+
+/*
+ * mxfp4_quantize_sr -- stochastic-rounding comparison arm ([P1]'s
+ * quick-read block and discussion: stochastic rounding diverges under full
+ * MXFP4 training; this operand lets its quantization error be measured).
+ *
+ * The E8M0 bytes are mxfp4_quantize's (same rule on the same rotated block
+ * maxima). Element codes: with y the rotated value, E its block's exponent
+ * and u its random integer, a = |y| 2^-E (exact, fp64); a >= 6 gives 6;
+ * otherwise, between the neighbouring E2M1 values g_lo <= a < g_hi, the
+ * magnitude is g_hi exactly when u < 2^32 (a - g_lo) / (g_hi - g_lo) (a
+ * probability equal to the distance, so the expected value is a) and g_lo
+ * otherwise; the sign bit is y's. rand_u32: DEVICE uint32 [rows][cols]
+ * (16-byte aligned, caller-owned), one per source element, element (r, c)
+ * using rand_u32[r][c] for either axis. A NULL rand_u32 with a non-empty
+ * shape returns MXFP4_ERR_NULL, a misaligned one MXFP4_ERR_ALIGN;
+ * otherwise errors as mxfp4_quantize (axis 2D32 returns MXFP4_ERR_MODE).
+ */
+int mxfp4_quantize_sr(const void* src_bf16, int64_t rows, int64_t cols, int axis,
+                      int hadamard, int scale_mode, const void* rand_u32, void* out_nibbles,
+                      void* out_e8m0, hipStream_t stream);
+
+/*
  * mxfp4_error_stats -- tensor-level decomposition of the MXFP4 error of the
  * operand mxfp4_quantize would produce ([P3] core insight: ideal scale
  * s* = m_b / 6, e = e_scale + e_DZ + e_grid, deadzone |x| < m_b / 24;

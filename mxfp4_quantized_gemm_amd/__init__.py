@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp4.so
 
 EXPORTS = (
     "mxfp4_quantize", "mxfp4_quantize_dual", "mxfp4_quantize_of", "mxfp4_quantize_mbs",
-    "mxfp4_error_stats", "mxfp4_gemm", "mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad",
+    "mxfp4_quantize_rs", "mxfp4_quantize_sr", "mxfp4_error_stats", "mxfp4_gemm", "mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad",
     "mxfp4_workspace_bytes", "mxfp4_status_string",
 )
 
@@ -60,6 +60,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mxfp4_quantize_of.restype = i32
     lib.mxfp4_quantize_mbs.argtypes = [p, i64, i64, i32, i32, i32, p, p, p, p]
     lib.mxfp4_quantize_mbs.restype = i32
+    lib.mxfp4_quantize_rs.argtypes = [p, i64, i64, i32, i32, i32, p, p, p, p]
+    lib.mxfp4_quantize_rs.restype = i32
+    lib.mxfp4_quantize_sr.argtypes = [p, i64, i64, i32, i32, i32, p, p, p, p]
+    lib.mxfp4_quantize_sr.restype = i32
     lib.mxfp4_error_stats.argtypes = [p, i64, i64, i32, i32, i32, p, sz, p, p]
     lib.mxfp4_error_stats.restype = i32
     lib.mxfp4_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
@@ -149,6 +153,35 @@ def mxfp4_quantize_of(src, rows, cols, axis, hadamard, scale_mode, out_nibbles, 
     _check(load_library().mxfp4_quantize_of(_ptr(src), rows, cols, axis, hadamard, scale_mode,
                                             _ptr(out_nibbles), _ptr(out_e8m0), _stream(stream)),
            "mxfp4_quantize_of")
+
+
+def mxfp4_quantize_rs(src, rows, cols, axis, hadamard, scale_mode, signs, out_nibbles, out_e8m0,
+                      stream=None):
+    """Random-sign Hadamard comparison arm: signs is a uint8 tensor with one
+    byte per index of the blocked axis (bit 0 set = flip)."""
+    import torch
+    _need(src, torch.bfloat16, rows * cols, "src")
+    _need(signs, torch.uint8, cols if axis == AXIS_ROW else rows, "signs")
+    _need(out_nibbles, torch.uint8, rows * cols // 2, "out_nibbles")
+    _need(out_e8m0, torch.uint8, rows * cols // 32, "out_e8m0")
+    _check(load_library().mxfp4_quantize_rs(_ptr(src), rows, cols, axis, hadamard, scale_mode,
+                                            _ptr(signs), _ptr(out_nibbles), _ptr(out_e8m0),
+                                            _stream(stream)), "mxfp4_quantize_rs")
+
+
+def mxfp4_quantize_sr(src, rows, cols, axis, hadamard, scale_mode, rand_u32, out_nibbles,
+                      out_e8m0, stream=None):
+    """Stochastic-rounding comparison arm: rand_u32 holds one 32-bit integer
+    per source element ([rows][cols], any 4-byte dtype, e.g. torch.int32)."""
+    import torch
+    _need(src, torch.bfloat16, rows * cols, "src")
+    _need(rand_u32, torch.uint32 if rand_u32.dtype == torch.uint32 else torch.int32, rows * cols,
+          "rand_u32")
+    _need(out_nibbles, torch.uint8, rows * cols // 2, "out_nibbles")
+    _need(out_e8m0, torch.uint8, rows * cols // 32, "out_e8m0")
+    _check(load_library().mxfp4_quantize_sr(_ptr(src), rows, cols, axis, hadamard, scale_mode,
+                                            _ptr(rand_u32), _ptr(out_nibbles), _ptr(out_e8m0),
+                                            _stream(stream)), "mxfp4_quantize_sr")
 
 
 def mxfp4_quantize_mbs(src, rows, cols, axis, hadamard, scale_mode, out_nibbles, out_e8m0,
@@ -277,6 +310,29 @@ def quantize_of(src, axis=AXIS_ROW, hadamard=16, scale_mode=SCALE_OCP_FLOOR, str
     nib = torch.empty((R, Kb), dtype=torch.uint8, device=src.device)
     sc = torch.empty((R, 2 * Kb // 32), dtype=torch.uint8, device=src.device)
     mxfp4_quantize_of(src, rows, cols, axis, hadamard, scale_mode, nib, sc, stream)
+    return nib, sc
+
+
+def quantize_rs(src, signs, axis=AXIS_ROW, hadamard=16, scale_mode=SCALE_OCP_FLOOR, stream=None):
+    """Allocate and compute the random-sign Hadamard operand (nibbles, e8m0)."""
+    import torch
+    rows, cols = src.shape
+    ns, ss = packed_shapes(rows, cols, axis)
+    nib = torch.empty(ns, dtype=torch.uint8, device=src.device)
+    sc = torch.empty(ss, dtype=torch.uint8, device=src.device)
+    mxfp4_quantize_rs(src, rows, cols, axis, hadamard, scale_mode, signs, nib, sc, stream)
+    return nib, sc
+
+
+def quantize_sr(src, rand_u32, axis=AXIS_ROW, hadamard=16, scale_mode=SCALE_OCP_FLOOR,
+                stream=None):
+    """Allocate and compute the stochastic-rounding operand (nibbles, e8m0)."""
+    import torch
+    rows, cols = src.shape
+    ns, ss = packed_shapes(rows, cols, axis)
+    nib = torch.empty(ns, dtype=torch.uint8, device=src.device)
+    sc = torch.empty(ss, dtype=torch.uint8, device=src.device)
+    mxfp4_quantize_sr(src, rows, cols, axis, hadamard, scale_mode, rand_u32, nib, sc, stream)
     return nib, sc
 
 

@@ -180,6 +180,32 @@ int mxfp4_quantize_mbs(const void* src_bf16, int64_t rows, int64_t cols, int axi
                                             out_nibbles, out_e8m0, out_mbs, stream));
 }
 
+int mxfp4_quantize_rs(const void* src_bf16, int64_t rows, int64_t cols, int axis, int hadamard,
+                      int scale_mode, const void* signs, void* out_nibbles, void* out_e8m0,
+                      hipStream_t stream) {
+  if (axis != MXFP4_AXIS_ROW && axis != MXFP4_AXIS_COL) return MXFP4_ERR_MODE;
+  const int st = check_quantize(src_bf16, rows, cols, axis, hadamard, scale_mode, out_nibbles,
+                                out_e8m0);
+  if (st != MXFP4_OK || rows == 0 || cols == 0) return st;
+  if (!signs) return MXFP4_ERR_NULL;
+  if (axis == MXFP4_AXIS_ROW && !aligned16(signs)) return MXFP4_ERR_ALIGN;
+  return hip_status(mx::launch_quantize_rs(src_bf16, rows, cols, axis, hadamard, scale_mode,
+                                           signs, out_nibbles, out_e8m0, stream));
+}
+
+int mxfp4_quantize_sr(const void* src_bf16, int64_t rows, int64_t cols, int axis, int hadamard,
+                      int scale_mode, const void* rand_u32, void* out_nibbles, void* out_e8m0,
+                      hipStream_t stream) {
+  if (axis != MXFP4_AXIS_ROW && axis != MXFP4_AXIS_COL) return MXFP4_ERR_MODE;
+  const int st = check_quantize(src_bf16, rows, cols, axis, hadamard, scale_mode, out_nibbles,
+                                out_e8m0);
+  if (st != MXFP4_OK || rows == 0 || cols == 0) return st;
+  if (!rand_u32) return MXFP4_ERR_NULL;
+  if (!aligned16(rand_u32)) return MXFP4_ERR_ALIGN;
+  return hip_status(mx::launch_quantize_sr(src_bf16, rows, cols, axis, hadamard, scale_mode,
+                                           rand_u32, out_nibbles, out_e8m0, stream));
+}
+
 int mxfp4_error_stats(const void* src_bf16, int64_t rows, int64_t cols, int axis, int hadamard,
                       int scale_mode, void* ws, size_t ws_bytes, double* out_stats,
                       hipStream_t stream) {

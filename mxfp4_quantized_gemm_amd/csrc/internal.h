@@ -28,6 +28,16 @@ hipError_t launch_quantize_mbs(const void* src, int64_t rows, int64_t cols, int 
                                int hadamard, int scale_mode, void* nib, void* sc, void* mbs,
                                hipStream_t stream);
 
+// Comparison arms: random-sign Hadamard (signs: one byte per index of the
+// blocked axis, bit 0 set = flip) and stochastic rounding (rnd: one uint32
+// per source element, [rows][cols]); axis ROW or COL.
+hipError_t launch_quantize_rs(const void* src, int64_t rows, int64_t cols, int axis, int hadamard,
+                              int scale_mode, const void* signs, void* nib, void* sc,
+                              hipStream_t stream);
+hipError_t launch_quantize_sr(const void* src, int64_t rows, int64_t cols, int axis, int hadamard,
+                              int scale_mode, const void* rnd, void* nib, void* sc,
+                              hipStream_t stream);
+
 // Tensor-level error decomposition sums (mxfp4_error_stats): ws holds
 // kStatsMaxGroups x 10 doubles of partial sums, out receives 10 doubles.
 constexpr int kStatsMaxGroups = 1024;

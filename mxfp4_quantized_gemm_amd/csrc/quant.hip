@@ -237,11 +237,12 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
 // scattered 16-byte and 1-byte stores. Four columns per lane keep the
 // register count low enough for several waves per SIMD, so the loads of one
 // wave overlap the arithmetic of another.
-template <int H, int MODE, int NB>
+template <int H, int MODE, int NB, bool RS = false>
 __global__ __launch_bounds__(64 * NB) void quant_col_staged_kernel(const uint16_t* __restrict__ src,
                                                                    int64_t rows, int64_t cols,
                                                                    uint8_t* __restrict__ nib,
-                                                                   uint8_t* __restrict__ sc) {
+                                                                   uint8_t* __restrict__ sc,
+                                                                   const uint8_t* __restrict__ signs) {
   __shared__ __attribute__((aligned(16))) uint8_t onib[256 * NB * 16];
   __shared__ __attribute__((aligned(16))) uint8_t osc[256 * NB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -255,6 +256,14 @@ __global__ __launch_bounds__(64 * NB) void quant_col_staged_kernel(const uint16_
     uint2 raw[32];
 #pragma unroll
     for (int r = 0; r < 32; ++r) raw[r] = ld_nt8(p + r * cols);
+    if constexpr (RS) {  // random-sign arm: one sign per row, the same for the whole wave
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        const uint32_t f = (signs[band * 32 + r] & 1u) ? 0x80008000u : 0u;
+        raw[r].x ^= f;
+        raw[r].y ^= f;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {  // one column at a time keeps the register count low
       float a[32];
@@ -297,18 +306,23 @@ __global__ __launch_bounds__(64 * NB) void quant_col_staged_kernel(const uint16_
 
 // Scalar path for any cols: one thread per (column, 32-row band); loads are
 // 2-byte, coalesced across the threads of a row.
-template <int H, int MODE>
+template <int H, int MODE, bool RS = false>
 __global__ __launch_bounds__(256) void quant_col_scalar_kernel(const uint16_t* __restrict__ src,
                                                                int64_t rows, int64_t cols,
                                                                uint8_t* __restrict__ nib,
-                                                               uint8_t* __restrict__ sc) {
+                                                               uint8_t* __restrict__ sc,
+                                                               const uint8_t* __restrict__ signs) {
   const int64_t ncg = (cols + 255) / 256;
   const int64_t c = ((int64_t)blockIdx.x % ncg) * 256 + threadIdx.x;
   const int64_t band = (int64_t)blockIdx.x / ncg;
   if (c >= cols || band * 32 >= rows) return;
   float v[32];
 #pragma unroll
-  for (int r = 0; r < 32; ++r) v[r] = __uint_as_float((uint32_t)src[(band * 32 + r) * cols + c] << 16);
+  for (int r = 0; r < 32; ++r) {
+    uint32_t b = (uint32_t)src[(band * 32 + r) * cols + c] << 16;
+    if constexpr (RS) b ^= (signs[band * 32 + r] & 1u) << 31;
+    v[r] = __uint_as_float(b);
+  }
   butterfly32<H>(v);
   uint4 out;
   uint32_t s;
@@ -863,12 +877,12 @@ hipError_t dispatch_axis(const void* src, int64_t rows, int64_t cols, int axis, 
       const int64_t grid = (rows / 256) * ((cols + 255) / 256);
       hipLaunchKernelGGL((quant_col_staged_kernel<H, MODE, 8>), dim3((unsigned)grid), dim3(512),
                          0, st, static_cast<const uint16_t*>(src), rows, cols,
-                         static_cast<uint8_t*>(nib), static_cast<uint8_t*>(sc));
+                         static_cast<uint8_t*>(nib), static_cast<uint8_t*>(sc), nullptr);
     } else if (rows % 128 == 0 && cols % 4 == 0 && ((uintptr_t)sc % 4 == 0)) {
       const int64_t grid = (rows / 128) * ((cols + 255) / 256);
       hipLaunchKernelGGL((quant_col_staged_kernel<H, MODE, 4>), dim3((unsigned)grid), blk, 0, st,
                          static_cast<const uint16_t*>(src), rows, cols,
-                         static_cast<uint8_t*>(nib), static_cast<uint8_t*>(sc));
+                         static_cast<uint8_t*>(nib), static_cast<uint8_t*>(sc), nullptr);
     } else if (cols % 8 == 0) {
       const int64_t grid = ((rows / 32 + 3) / 4) * ((cols + 511) / 512);
       hipLaunchKernelGGL((quant_col_kernel<H, MODE>), dim3((unsigned)grid), blk, 0, st,
@@ -878,7 +892,7 @@ hipError_t dispatch_axis(const void* src, int64_t rows, int64_t cols, int axis, 
       const int64_t grid = (rows / 32) * ((cols + 255) / 256);
       hipLaunchKernelGGL((quant_col_scalar_kernel<H, MODE>), dim3((unsigned)grid), blk, 0, st,
                          static_cast<const uint16_t*>(src), rows, cols,
-                         static_cast<uint8_t*>(nib), static_cast<uint8_t*>(sc));
+                         static_cast<uint8_t*>(nib), static_cast<uint8_t*>(sc), nullptr);
     }
   } else {
     const int64_t grid = (rows / 32) * ((cols / 32 + 7) / 8);
@@ -915,6 +929,192 @@ hipError_t dispatch_dual(const void* src, int64_t rows, int64_t cols, void* rnib
   // take 68 KB of LDS per work-group and leave too few waves per CU.
   hipLaunchKernelGGL((quant_dual_kernel<H, MODE, 4>), dim3((unsigned)((rows / 128) * (cols / 256))),
                      dim3(256), 0, st, s16, rows, cols, rn, rs, cn, cs);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------ comparison arms
+// [P1] reports that random Hadamard transforms and stochastic rounding
+// diverge under full MXFP4 training (quick-read block and discussion); these
+// arms quantize with them so their error can be measured beside the
+// deterministic H16 + round-to-nearest operand. The random numbers are
+// inputs.
+//
+// Random signs (RS): the operand of diag(s) x, s_i = -1 where bit 0 of
+// signs[i] is set, i along the blocked axis; a bf16 sign flip is exact, so
+// the kernels flip the loaded bits and then run the plain rotation and
+// encode. Row blocks: one thread per 32-block (the block's 32 sign bytes
+// come from L2; every row shares them). Column blocks: the column kernels
+// with their RS flag (one sign per row, the same for a whole wave).
+template <int H, int MODE>
+__global__ __launch_bounds__(256) void quant_rs_row_kernel(const uint4* __restrict__ src,
+                                                           int64_t nblocks, int64_t ncb,
+                                                           const uint4* __restrict__ signs,
+                                                           uint4* __restrict__ nib,
+                                                           uint8_t* __restrict__ sc) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  const int64_t cb = b % ncb;
+  const uint4 s0 = signs[cb * 2], s1 = signs[cb * 2 + 1];
+  const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  uint4 q[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    q[j] = src[b * 4 + j];
+    // bf16 dword k of the block holds elements 2k, 2k + 1; sign byte i sits
+    // in sw[i / 4] at bit 8 (i % 4)
+    uint32_t* d = reinterpret_cast<uint32_t*>(&q[j]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int k = 4 * j + t;
+      const uint32_t w = sw[k >> 1] >> (16 * (k & 1));
+      d[t] ^= ((w & 1u) << 15) | (((w >> 8) & 1u) << 31);
+    }
+  }
+  float v[32];
+  unpack64B(q, v);
+  butterfly32<H>(v);
+  uint4 out;
+  uint32_t s;
+  encode_block_sh<MODE, kScaleShift<H>>(v, out, s);
+  nib[b] = out;
+  sc[b] = (uint8_t)s;
+}
+
+// Stochastic rounding (SR) of one rotated value y in a finite block with
+// E8M0 byte s (E = s - 127), with one uniform 32-bit integer u: a = |y| 2^-E
+// (exact in fp64); below 6, between the neighbouring grid values
+// g_lo <= a < g_hi, round up exactly when u < p 2^32 with
+// p = (a - g_lo) / (g_hi - g_lo) (exact: the gap is 0.5, 1 or 2), i.e. with
+// probability p; a >= 6 gives 6. Returns the 4-bit code (sign of y kept).
+__device__ __forceinline__ uint32_t sr_code(float y, uint32_t s, uint32_t u) {
+  const double inv = __longlong_as_double((long long)((int64_t)(1150u - s) << 52));  // 2^-E
+  const double a = fabs((double)y) * inv;
+  const int lo = (a >= 0.5) + (a >= 1.0) + (a >= 1.5) + (a >= 2.0) + (a >= 3.0) + (a >= 4.0) +
+                 (a >= 6.0);
+  const double glo = lo < 4 ? 0.5 * lo : (lo == 4 ? 2.0 : (lo == 5 ? 3.0 : 4.0));
+  const double inv_gap = lo < 4 ? 2.0 : (lo < 6 ? 1.0 : 0.5);
+  const double thr = (a - glo) * inv_gap * 4294967296.0;
+  const uint32_t mag = lo >= 7 ? 7u : (uint32_t)lo + ((double)u < thr ? 1u : 0u);
+  return mag | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+// 32 rotated values and their 32 random integers -> (nibbles, scale byte),
+// with the E8M0 rule of the round-to-nearest operand.
+template <int MODE>
+__device__ __forceinline__ void sr_block(const float (&v)[32], const uint32_t (&u)[32], uint4& nib,
+                                         uint32_t& s) {
+  s = e8m0_byte<MODE>(amax_bits_n<32>(v));
+  if (s == 255u) {
+    nib = make_uint4(0, 0, 0, 0);
+    return;
+  }
+  uint32_t w[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t r = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r |= sr_code(v[8 * d + k], s, u[8 * d + k]) << (4 * k);
+    w[d] = r;
+  }
+  nib = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// SR, row blocks: one thread per 32-block (64 source bytes, 128 random bytes).
+template <int H, int MODE>
+__global__ __launch_bounds__(256) void quant_sr_row_kernel(const uint4* __restrict__ src,
+                                                           int64_t nblocks,
+                                                           const uint4* __restrict__ rnd,
+                                                           uint4* __restrict__ nib,
+                                                           uint8_t* __restrict__ sc) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  uint4 q[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) q[j] = src[b * 4 + j];
+  uint32_t u[32];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint4 t = rnd[b * 8 + j];
+    u[4 * j] = t.x; u[4 * j + 1] = t.y; u[4 * j + 2] = t.z; u[4 * j + 3] = t.w;
+  }
+  float v[32];
+  unpack64B(q, v);
+  hadamard32<H>(v);
+  uint4 out;
+  uint32_t s;
+  sr_block<MODE>(v, u, out, s);
+  nib[b] = out;
+  sc[b] = (uint8_t)s;
+}
+
+// SR, column blocks: one thread per (column, 32-row band); source and random
+// loads are coalesced across the threads of a row.
+template <int H, int MODE>
+__global__ __launch_bounds__(256) void quant_sr_col_kernel(const uint16_t* __restrict__ src,
+                                                           int64_t rows, int64_t cols,
+                                                           const uint32_t* __restrict__ rnd,
+                                                           uint8_t* __restrict__ nib,
+                                                           uint8_t* __restrict__ sc) {
+  const int64_t ncg = (cols + 255) / 256;
+  const int64_t c = ((int64_t)blockIdx.x % ncg) * 256 + threadIdx.x;
+  const int64_t band = (int64_t)blockIdx.x / ncg;
+  if (c >= cols || band * 32 >= rows) return;
+  float v[32];
+  uint32_t u[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    const int64_t e = (band * 32 + r) * cols + c;
+    v[r] = __uint_as_float((uint32_t)src[e] << 16);
+    u[r] = rnd[e];
+  }
+  hadamard32<H>(v);
+  uint4 out;
+  uint32_t s;
+  sr_block<MODE>(v, u, out, s);
+  *reinterpret_cast<uint4*>(nib + c * (rows / 2) + band * 16) = out;
+  sc[c * (rows / 32) + band] = (uint8_t)s;
+}
+
+template <int H, int MODE>
+hipError_t dispatch_rs(const void* src, int64_t rows, int64_t cols, int axis, const void* signs,
+                       void* nib, void* sc, hipStream_t st) {
+  const auto* sg = static_cast<const uint8_t*>(signs);
+  if (axis == 0) {
+    const int64_t ncb = cols / 32, nblocks = rows * ncb;
+    hipLaunchKernelGGL((quant_rs_row_kernel<H, MODE>), dim3((unsigned)((nblocks + 255) / 256)),
+                       dim3(256), 0, st, static_cast<const uint4*>(src), nblocks, ncb,
+                       static_cast<const uint4*>(signs), static_cast<uint4*>(nib),
+                       static_cast<uint8_t*>(sc));
+  } else if (rows % 128 == 0 && cols % 4 == 0 && (uintptr_t)sc % 4 == 0) {
+    const int64_t grid = (rows / 128) * ((cols + 255) / 256);
+    hipLaunchKernelGGL((quant_col_staged_kernel<H, MODE, 4, true>), dim3((unsigned)grid),
+                       dim3(256), 0, st, static_cast<const uint16_t*>(src), rows, cols,
+                       static_cast<uint8_t*>(nib), static_cast<uint8_t*>(sc), sg);
+  } else {
+    const int64_t grid = (rows / 32) * ((cols + 255) / 256);
+    hipLaunchKernelGGL((quant_col_scalar_kernel<H, MODE, true>), dim3((unsigned)grid), dim3(256),
+                       0, st, static_cast<const uint16_t*>(src), rows, cols,
+                       static_cast<uint8_t*>(nib), static_cast<uint8_t*>(sc), sg);
+  }
+  return hipGetLastError();
+}
+
+template <int H, int MODE>
+hipError_t dispatch_sr(const void* src, int64_t rows, int64_t cols, int axis, const void* rnd,
+                       void* nib, void* sc, hipStream_t st) {
+  if (axis == 0) {
+    const int64_t nblocks = rows * (cols / 32);
+    hipLaunchKernelGGL((quant_sr_row_kernel<H, MODE>), dim3((unsigned)((nblocks + 255) / 256)),
+                       dim3(256), 0, st, static_cast<const uint4*>(src), nblocks,
+                       static_cast<const uint4*>(rnd), static_cast<uint4*>(nib),
+                       static_cast<uint8_t*>(sc));
+  } else {
+    const int64_t grid = (rows / 32) * ((cols + 255) / 256);
+    hipLaunchKernelGGL((quant_sr_col_kernel<H, MODE>), dim3((unsigned)grid), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(src), rows, cols,
+                       static_cast<const uint32_t*>(rnd), static_cast<uint8_t*>(nib),
+                       static_cast<uint8_t*>(sc));
+  }
   return hipGetLastError();
 }
 
@@ -967,6 +1167,34 @@ hipError_t launch_quantize_mbs(const void* src, int64_t rows, int64_t cols, int 
                          : dispatch_mbs<32, kOcpFloor>(src, rows, cols, axis, nib, sc, mbs, stream);
     default: return ceil ? dispatch_mbs<0, kCeil>(src, rows, cols, axis, nib, sc, mbs, stream)
                          : dispatch_mbs<0, kOcpFloor>(src, rows, cols, axis, nib, sc, mbs, stream);
+  }
+}
+
+hipError_t launch_quantize_rs(const void* src, int64_t rows, int64_t cols, int axis, int hadamard,
+                              int scale_mode, const void* signs, void* nib, void* sc,
+                              hipStream_t stream) {
+  const bool ceil = scale_mode == kCeil;
+  switch (hadamard) {
+    case 16: return ceil ? dispatch_rs<16, kCeil>(src, rows, cols, axis, signs, nib, sc, stream)
+                         : dispatch_rs<16, kOcpFloor>(src, rows, cols, axis, signs, nib, sc, stream);
+    case 32: return ceil ? dispatch_rs<32, kCeil>(src, rows, cols, axis, signs, nib, sc, stream)
+                         : dispatch_rs<32, kOcpFloor>(src, rows, cols, axis, signs, nib, sc, stream);
+    default: return ceil ? dispatch_rs<0, kCeil>(src, rows, cols, axis, signs, nib, sc, stream)
+                         : dispatch_rs<0, kOcpFloor>(src, rows, cols, axis, signs, nib, sc, stream);
+  }
+}
+
+hipError_t launch_quantize_sr(const void* src, int64_t rows, int64_t cols, int axis, int hadamard,
+                              int scale_mode, const void* rnd, void* nib, void* sc,
+                              hipStream_t stream) {
+  const bool ceil = scale_mode == kCeil;
+  switch (hadamard) {
+    case 16: return ceil ? dispatch_sr<16, kCeil>(src, rows, cols, axis, rnd, nib, sc, stream)
+                         : dispatch_sr<16, kOcpFloor>(src, rows, cols, axis, rnd, nib, sc, stream);
+    case 32: return ceil ? dispatch_sr<32, kCeil>(src, rows, cols, axis, rnd, nib, sc, stream)
+                         : dispatch_sr<32, kOcpFloor>(src, rows, cols, axis, rnd, nib, sc, stream);
+    default: return ceil ? dispatch_sr<0, kCeil>(src, rows, cols, axis, rnd, nib, sc, stream)
+                         : dispatch_sr<0, kOcpFloor>(src, rows, cols, axis, rnd, nib, sc, stream);
   }
 }
 

@@ -143,6 +143,25 @@ def test_quantize_of_validation(lib):
     assert call(rows=0, src=NULL, nib=NULL, sc=NULL) == 0
 
 
+def test_quantize_rs_and_sr_validation(lib):
+    for fn in (lib.mxfp4_quantize_rs, lib.mxfp4_quantize_sr):
+        call = lambda **kw: fn(kw.get("src", FAKE), kw.get("rows", 64), kw.get("cols", 64),
+                               kw.get("axis", 0), kw.get("h", 16), kw.get("mode", 0),
+                               kw.get("aux", FAKE), kw.get("nib", FAKE), kw.get("sc", FAKE), NULL)
+        assert call(axis=2) == 3
+        assert call(h=8) == 3
+        assert call(mode=2) == 3
+        assert call(cols=40) == 2
+        assert call(axis=1, rows=40) == 2
+        assert call(aux=NULL) == 1
+        assert call(nib=NULL) == 1
+        assert call(src=FAKE_ODD) == 6
+        assert call(rows=0, src=NULL, aux=NULL, nib=NULL, sc=NULL) == 0
+    # row-axis signs are read 16 bytes at a time; random integers always are
+    assert lib.mxfp4_quantize_rs(FAKE, 64, 64, 0, 16, 0, FAKE_ODD, FAKE, FAKE, NULL) == 6
+    assert lib.mxfp4_quantize_sr(FAKE, 64, 64, 1, 16, 0, FAKE_ODD, FAKE, FAKE, NULL) == 6
+
+
 def test_quantize_mbs_validation(lib):
     call = lambda **kw: lib.mxfp4_quantize_mbs(kw.get("src", FAKE), kw.get("rows", 128),
                                                kw.get("cols", 128), kw.get("axis", 0),
