@@ -169,10 +169,11 @@ int mxfp4_quantize_mbs(const void* src_bf16, int64_t rows, int64_t cols, int axi
 
 /*
  * mxfp4_quantize_rs -- random-sign Hadamard comparison arm. [P1]'s
- * quick-read block and discussion report that random Hadamard transforms
- * (random sign flips before the rotation) diverge under full MXFP4
- * training, where the deterministic H16 trains; this entry point produces
- * such an operand so that its quantization error can be measured.
+ * quick-read block, section A.2 and hypothesis H2 report that random
+ * Hadamard transforms (random sign flips before the rotation) diverge
+ * under full MXFP4 training, where the deterministic H16 trains; this entry
+ * point produces such an operand so that its quantization error can be
+ * measured.
  *
  * Writes exactly what mxfp4_quantize (axis ROW or COL) writes for diag(s)
  * src, s_i = -1 where bit 0 of signs[i] is set and +1 where it is clear,
@@ -190,7 +191,7 @@ int mxfp4_quantize_rs(const void* src_bf16, int64_t rows, int64_t cols, int axis
 
 /*
  * mxfp4_quantize_sr -- stochastic-rounding comparison arm ([P1]'s
- * quick-read block and discussion: stochastic rounding diverges under full
+ * quick-read block and hypothesis H2: stochastic rounding diverges under full
  * MXFP4 training; this operand lets its quantization error be measured).
  *
  * The E8M0 bytes are mxfp4_quantize's (same rule on the same rotated block

@@ -934,8 +934,9 @@ hipError_t dispatch_dual(const void* src, int64_t rows, int64_t cols, void* rnib
 
 // ------------------------------------------------ comparison arms
 // [P1] reports that random Hadamard transforms and stochastic rounding
-// diverge under full MXFP4 training (quick-read block and discussion); these
-// arms quantize with them so their error can be measured beside the
+// diverge under full MXFP4 training (quick-read block, section A.2,
+// hypothesis H2); these arms quantize with them so their error can be
+// measured beside the
 // deterministic H16 + round-to-nearest operand. The random numbers are
 // inputs.
 //

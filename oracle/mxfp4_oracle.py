@@ -226,8 +226,8 @@ def quantize_chunked(src_bf16: np.ndarray, axis: int, hadamard: int, mode: int,
 
 # --------------------------------------------------------------------------
 # Error-only comparison arms that [P1] reports as diverging under full MXFP4
-# training (quick-read block and discussion: random Hadamard transforms and
-# stochastic rounding). They are built here to measure their quantization
+# training (quick-read block, section A.2, hypothesis H2: random Hadamard
+# transforms and stochastic rounding). They are built here to measure their quantization
 # error next to the deterministic H16 + round-to-nearest path; the random
 # numbers are inputs.
 # --------------------------------------------------------------------------
