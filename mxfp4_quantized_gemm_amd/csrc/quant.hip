@@ -936,9 +936,8 @@ hipError_t dispatch_dual(const void* src, int64_t rows, int64_t cols, void* rnib
 // [P1] reports that random Hadamard transforms and stochastic rounding
 // diverge under full MXFP4 training (quick-read block, section A.2,
 // hypothesis H2); these arms quantize with them so their error can be
-// measured beside the
-// deterministic H16 + round-to-nearest operand. The random numbers are
-// inputs.
+// measured beside the deterministic H16 + round-to-nearest operand. The
+// random numbers are inputs.
 //
 // Random signs (RS): the operand of diag(s) x, s_i = -1 where bit 0 of
 // signs[i] is set, i along the blocked axis; a bf16 sign flip is exact, so
