@@ -395,10 +395,10 @@ def main():
             fn()
             ev[s][i + 1].record(stream)
     torch.cuda.synchronize()
-    kernel_ms = np.zeros(len(seq))
-    for s in range(K_):
-        kernel_ms += np.array([ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(len(seq))])
-    kernel_ms /= K_
+    D = np.array([[ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(len(seq))]
+                  for s in range(K_)])
+    kernel_ms = D.mean(axis=0)
+    kernel_med, kernel_min = np.median(D, axis=0), D.min(axis=0)
 
     per_product = {}
     kernels = []
@@ -412,7 +412,9 @@ def main():
             rec["quant_" + "AB"[j] + "_us"] = round(kernel_ms[idx] * 1e3, 2)
             rec["quant_" + "AB"[j] + "_GBs"] = round(gbs, 1)
             kernels.append({"kernel": f"{name}.quant_{'AB'[j]}", "axis": ["row", "col", "2d"][axis],
-                            "us": round(kernel_ms[idx] * 1e3, 2), "GB/s": round(gbs, 1),
+                            "us": round(kernel_ms[idx] * 1e3, 2),
+                            "us_median": round(kernel_med[idx] * 1e3, 2),
+                            "us_min": round(kernel_min[idx] * 1e3, 2), "GB/s": round(gbs, 1),
                             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
         else:
             f = 2.0 * p["GM"] * p["GN"] * p["GK"]
@@ -422,6 +424,8 @@ def main():
             tot = kernel_ms[idx - 2] + kernel_ms[idx - 1] + kernel_ms[idx]
             rec["fused_TFLOPs"] = round(f / (tot * 1e-3) / 1e12, 1)
             kernels.append({"kernel": f"{name}.gemm", "us": round(kernel_ms[idx] * 1e3, 2),
+                            "us_median": round(kernel_med[idx] * 1e3, 2),
+                            "us_min": round(kernel_min[idx] * 1e3, 2),
                             "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / MXFP4_PEAK_TFLOPS, 4)})
     log(f"step {ms_per_step:.3f} ms, {value:.1f} TFLOP/s")
 
