@@ -519,14 +519,15 @@ def main():
                      quant[f"col_h16_{['ocp_floor', 'ceil'][m]}"]["us"]) / (mean_ms * 1e3), 3)
             del outs
         # outlier fallback: q1 and the half-residual q2 in one pass (2x the output)
-        for m in (0, 1):
-            outs = [(torch.empty((R, Cc), dtype=torch.uint8, device=dev),
-                     torch.empty((R, 2 * Cc // 32), dtype=torch.uint8, device=dev))
+        for ax, m in ((0, 0), (0, 1), (1, 0)):
+            Ro, Ko = (R, Cc) if ax == 0 else (Cc, R)
+            outs = [(torch.empty((Ro, Ko), dtype=torch.uint8, device=dev),
+                     torch.empty((Ro, 2 * Ko // 32), dtype=torch.uint8, device=dev))
                     for _ in range(nsets)]
 
             def qo(i):
                 k = i % nsets
-                mx.mxfp4_quantize_of(srcs[k], R, Cc, 0, 16, m, outs[k][0], outs[k][1], stream)
+                mx.mxfp4_quantize_of(srcs[k], R, Cc, ax, 16, m, outs[k][0], outs[k][1], stream)
             for i in range(10):
                 qo(i)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -537,7 +538,7 @@ def main():
             torch.cuda.synchronize()
             mean_ms = e0.elapsed_time(e1) / its
             b = R * Cc * (2 + 2 * (0.5 + 1 / 32))
-            quant[f"of_row_h16_{['ocp_floor', 'ceil'][m]}"] = {
+            quant[f"of_{['row', 'col'][ax]}_h16_{['ocp_floor', 'ceil'][m]}"] = {
                 "us": round(mean_ms * 1e3, 2), "GB/s": round(b / (mean_ms * 1e-3) / 1e9, 1),
                 "frac_hbm": round(b / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
             del outs

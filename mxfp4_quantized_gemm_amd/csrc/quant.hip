@@ -628,6 +628,69 @@ __global__ __launch_bounds__(256) void quant_of_col_kernel(const uint16_t* __res
   sc[c * 2 * nb + nb + band] = (uint8_t)s2;
 }
 
+// Column axis, staged (rows % 128 == 0, cols % 4 == 0, nibble pointer
+// 16-byte and scale pointer 4-byte aligned): the column quantizer's tile
+// with 4 bands (128 rows x 256 columns per work-group, 8-byte non-temporal
+// loads, a lane's 4 columns of its band in registers); both passes of every
+// block are staged in LDS and leave as 64-byte nibble runs and 4-byte scale
+// words per column and half.
+template <int H, int MODE>
+__global__ __launch_bounds__(256) void quant_of_col_staged_kernel(const uint16_t* __restrict__ src,
+                                                                  int64_t rows, int64_t cols,
+                                                                  uint8_t* __restrict__ nib,
+                                                                  uint8_t* __restrict__ sc) {
+  constexpr int NB = 4;
+  __shared__ __attribute__((aligned(16))) uint8_t onib[2][256 * NB * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t osc[2][256 * NB];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t ncg = (cols + 255) / 256;
+  const int64_t cg = (int64_t)blockIdx.x % ncg;
+  const int64_t rg = (int64_t)blockIdx.x / ncg;
+  const int64_t c0 = cg * 256 + (int64_t)lane * 4;
+  if (c0 < cols) {
+    const uint16_t* p = src + (rg * NB + wave) * 32 * cols + c0;
+    uint2 raw[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) raw[r] = ld_nt8(p + r * cols);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float a[32];
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        const uint32_t d = j < 2 ? raw[r].x : raw[r].y;
+        a[r] = (j & 1) ? bf16hi(d) : bf16lo(d);
+      }
+      hadamard32<H>(a);
+      uint4 n1, n2;
+      uint32_t s1, s2;
+      of_block<MODE>(a, n1, s1, n2, s2);
+      const int k = (lane * 4 + j) * NB + wave;
+      *reinterpret_cast<uint4*>(onib[0] + k * 16) = n1;
+      *reinterpret_cast<uint4*>(onib[1] + k * 16) = n2;
+      osc[0][k] = (uint8_t)s1;
+      osc[1][k] = (uint8_t)s2;
+    }
+  }
+  __syncthreads();
+  // output row c: q1's rows / 2 nibble bytes, then q2's; scales likewise
+  const int64_t npitch = rows, spitch = rows / 16, nhalf = rows / 2, shalf = rows / 32;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = threadIdx.x + 64 * NB * i;  // 16-byte chunk: column k / NB, band k % NB
+      const int64_t col = cg * 256 + k / NB;
+      if (col < cols)
+        *reinterpret_cast<uint4*>(nib + col * npitch + h * nhalf + rg * 16 * NB + (k % NB) * 16) =
+            *reinterpret_cast<const uint4*>(onib[h] + k * 16);
+    }
+    const int64_t col = cg * 256 + threadIdx.x;
+    if (col < cols)
+      *reinterpret_cast<uint32_t*>(sc + col * spitch + h * shalf + rg * NB) =
+          *reinterpret_cast<const uint32_t*>(osc[h] + threadIdx.x * NB);
+  }
+}
+
 template <int H, int MODE>
 hipError_t dispatch_of(const void* src, int64_t rows, int64_t cols, int axis, void* nib, void* sc,
                        hipStream_t st) {
@@ -636,6 +699,12 @@ hipError_t dispatch_of(const void* src, int64_t rows, int64_t cols, int axis, vo
     hipLaunchKernelGGL((quant_of_row_kernel<H, MODE>), dim3((unsigned)((nblocks + 255) / 256)),
                        dim3(256), 0, st, static_cast<const uint4*>(src), nblocks, ncb,
                        static_cast<uint8_t*>(nib), static_cast<uint8_t*>(sc));
+  } else if (rows % 128 == 0 && cols % 4 == 0 && (uintptr_t)nib % 16 == 0 &&
+             (uintptr_t)sc % 4 == 0) {
+    const int64_t grid = (rows / 128) * ((cols + 255) / 256);
+    hipLaunchKernelGGL((quant_of_col_staged_kernel<H, MODE>), dim3((unsigned)grid), dim3(256), 0,
+                       st, static_cast<const uint16_t*>(src), rows, cols, static_cast<uint8_t*>(nib),
+                       static_cast<uint8_t*>(sc));
   } else {
     const int64_t grid = (rows / 32) * ((cols + 255) / 256);
     hipLaunchKernelGGL((quant_of_col_kernel<H, MODE>), dim3((unsigned)grid), dim3(256), 0, st,

@@ -35,7 +35,12 @@ def assert_of_same(bits, axis, h, mode, what):
 @pytest.mark.parametrize("h", [0, 16, 32])
 @pytest.mark.parametrize("mode", [0, 1])
 def test_small_shapes_bit_exact(axis, h, mode):
-    for i, (r, c) in enumerate([(32, 32), (64, 96), (96, 320), (256, 512), (33 * 32, 64)]):
+    # column axis: the staged kernel for rows % 128 == 0 and cols % 4 == 0
+    # ((256, 512), (384, 100), (128, 260)), the per-column kernel otherwise
+    shapes = [(32, 32), (64, 96), (96, 320), (256, 512), (33 * 32, 64)]
+    if axis == 1:
+        shapes += [(384, 100), (128, 260)]
+    for i, (r, c) in enumerate(shapes):
         assert_of_same(heavy(r, c, 9100 + 7 * i + axis), axis, h, mode,
                        f"axis={axis} h={h} mode={mode} shape={(r, c)}")
 
@@ -43,13 +48,18 @@ def test_small_shapes_bit_exact(axis, h, mode):
 @pytest.mark.parametrize("axis", [0, 1])
 @pytest.mark.parametrize("mode", [0, 1])
 def test_edge_values_bit_exact(axis, mode):
-    for h in (0, 16, 32):
-        assert_of_same(edge_matrix(128, 256, seed=17), axis, h, mode, f"edge axis={axis} h={h}")
+    mats = [edge_matrix(128, 256, seed=17)]
+    if axis == 1:  # special blocks down the columns as well
+        mats.append(np.ascontiguousarray(edge_matrix(256, 128, seed=18).T))
+    for k, bits in enumerate(mats):
+        for h in (0, 16, 32):
+            assert_of_same(bits, axis, h, mode, f"edge {k} axis={axis} h={h}")
 
 
-def test_quantizer_workload_full_size():
+@pytest.mark.parametrize("axis", [0, 1])
+def test_quantizer_workload_full_size(axis):
     A = synthetic.make("quant")["A"]
-    assert_of_same(A, 0, 16, 1, "full row ceil")
+    assert_of_same(A, axis, 16, 1, f"full axis={axis} ceil")
 
 
 @pytest.mark.parametrize("mode", [0, 1])
