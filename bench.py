@@ -109,12 +109,13 @@ def cpu_baseline(work, budget_rows=2048, budget_cols=8192):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
         cores = 1
-    flops = 0.0
+    flops = qbytes = tq = 0.0
     t0 = time.perf_counter()
     for name, wl, op, (T, N, K), (pn, qn) in PRODUCTS:
         P, Q = work[wl][pn], work[wl][qn]
         (_, _), (_, _), (GM, GN, GK) = plan(op, T, N, K)
         m, n = min(budget_rows, GM), min(budget_cols, GN)
+        tq0 = time.perf_counter()
         if op == "fprop":
             qa = O.quantize(P[:m], O.AXIS_ROW, 16, 0)
             qb = O.quantize(Q[:n], O.AXIS_ROW, 16, 0)
@@ -124,11 +125,15 @@ def cpu_baseline(work, budget_rows=2048, budget_cols=8192):
         else:
             qa = O.quantize(np.ascontiguousarray(P[:, :m]), O.AXIS_COL, 16, 0)
             qb = O.quantize(np.ascontiguousarray(Q[:, :n]), O.AXIS_COL, 16, 0)
+        tq += time.perf_counter() - tq0
+        qbytes += (m + n) * GK * (2 + 0.5 + 1 / 32)
         O.gemm_ref(O.dequantize(*qa), O.dequantize(*qb))
         flops += 2.0 * m * n * GK
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "seconds": round(dt, 3),
+            "quantize_GB/s": round(qbytes / tq / 1e9, 3),
+            "gemm_GFLOP/s": round(flops / (dt - tq) / 1e9, 1),
             "sample": f"{budget_rows}x{budget_cols} output tile of each of the 4 products at full "
                       f"reduction length: oracle rotate+quantize of the matching source slices, "
                       f"dequantize, fp64 GEMM and sum|a||b| (numpy; BLAS threads = {cores})"}
