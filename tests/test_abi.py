@@ -261,3 +261,15 @@ def test_product_path_does_not_import_oracle():
                 with open(os.path.join(dirpath, fn)) as f:
                     text = f.read()
                 assert not re.search(r"\boracle\b", text), fn
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The bench measures one GPU: --gpus 2 exits (status 2) with a message,
+    before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
