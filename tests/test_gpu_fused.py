@@ -155,12 +155,14 @@ def test_qkv_fprop_full(qkv, out_dtype):
     sampled_check("fprop", qkv["X"], qkv["W"], 8192, 6144, 4096, 16, 0, out_dtype)
 
 
-def test_mlp_gate_up_fprop_full(mlp):
-    sampled_check("fprop", mlp["X"], mlp["W_gu"], 8192, 28672, 4096, 16, 0, 0)
+@pytest.mark.parametrize("out_dtype", [0, 1])
+def test_mlp_gate_up_fprop_full(mlp, out_dtype):
+    sampled_check("fprop", mlp["X"], mlp["W_gu"], 8192, 28672, 4096, 16, 0, out_dtype)
 
 
-def test_mlp_down_dgrad_full(mlp):
-    sampled_check("dgrad", mlp["dY"], mlp["W_down"], 8192, 4096, 14336, 16, 0, 0)
+@pytest.mark.parametrize("h,mode,out_dtype", [(16, 0, 0), (16, 1, 1), (32, 0, 0), (0, 1, 0)])
+def test_mlp_down_dgrad_full(mlp, h, mode, out_dtype):
+    sampled_check("dgrad", mlp["dY"], mlp["W_down"], 8192, 4096, 14336, h, mode, out_dtype)
 
 
 @pytest.mark.parametrize("h", [16, 32, 0])
@@ -170,3 +172,7 @@ def test_down_wgrad_full(down_wgrad, h):
 
 def test_down_wgrad_full_ceil(down_wgrad):
     sampled_check("wgrad", down_wgrad["dY"], down_wgrad["X"], 8192, 4096, 14336, 16, 1, 0)
+
+
+def test_down_wgrad_full_bf16_out(down_wgrad):
+    sampled_check("wgrad", down_wgrad["dY"], down_wgrad["X"], 8192, 4096, 14336, 16, 1, 1)

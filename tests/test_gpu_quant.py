@@ -186,6 +186,6 @@ def test_dual_edge_values_bit_exact(h, mode):
     assert_dual_same(bits, h, mode, f"dual edge h={h} mode={mode}")
 
 
-@pytest.mark.parametrize("mode", [0, 1])
-def test_dual_quantizer_workload_full_size(quant_workload, mode):
-    assert_dual_same(quant_workload, 16, mode, f"dual full mode={mode}")
+@pytest.mark.parametrize("h,mode", [(16, 0), (16, 1), (32, 0), (0, 1)])
+def test_dual_quantizer_workload_full_size(quant_workload, h, mode):
+    assert_dual_same(quant_workload, h, mode, f"dual full h={h} mode={mode}")
