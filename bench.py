@@ -450,6 +450,25 @@ def main():
     torch.cuda.synchronize()
     fused_ms = e0.elapsed_time(e1) / K_
 
+    # the same GEMMs with bf16 output (C written in bf16, RNE), K launches each
+    for p in prods:
+        cb = torch.empty((p["GM"], p["GN"]), dtype=torch.bfloat16, device=dev)
+        g = lambda: mx.mxfp4_gemm(p["an"], p["asc"], p["bn"], p["bsc"], p["GM"], p["GN"], p["GK"],
+                                  cb, mx.OUT_BF16, stream)
+        for _ in range(3):
+            g()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K_):
+            g()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / K_ * 1e3
+        rec = per_product[p["name"]]
+        rec["gemm_bf16_out_us"] = round(us, 2)
+        rec["gemm_bf16_out_TFLOPs"] = round(2.0 * p["GM"] * p["GN"] * p["GK"] / (us * 1e-6) / 1e12, 1)
+        del cb
+
     # -------------------------------------------------- quantizer workload
     quant = None
     if not args.no_quantizer:
