@@ -479,7 +479,8 @@ def main():
             srcs.append(srcs[0].clone())
         R, Cc = A.shape
         quant = {}
-        arms = [(ax, 16, m) for ax in (0, 1, 2) for m in (0, 1)] + [(0, 0, 0), (0, 32, 0)]
+        arms = [(ax, 16, m) for ax in (0, 1, 2) for m in (0, 1)] + [(0, 0, 0), (0, 32, 0), (1, 0, 0),
+                                                                   (1, 32, 0)]
         its = args.quant_iters
         for ax, h, m in arms:
             ns_, ss_ = mx.packed_shapes(R, Cc, ax)
