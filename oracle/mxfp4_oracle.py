@@ -259,19 +259,15 @@ def quantize_rs(src_bf16: np.ndarray, axis: int, hadamard: int, mode: int,
 def sr_codes(y: np.ndarray, E: np.ndarray, rnd: np.ndarray) -> np.ndarray:
     """Stochastic-rounding codes (sign << 3 | magnitude) of y / 2^E.
 
-    a = |fl32(y 2^-E)| (one fp32 multiply by the power of two, exact unless
-    the product falls below the fp32 normal range). Below 6, with
-    g_lo <= a < g_hi the two neighbouring grid values,
-    p = (a - g_lo) / (g_hi - g_lo) (exact: the gap is 0.5, 1 or 2) and the
-    magnitude rounds up to g_hi exactly when rnd < p 2^32, i.e. with
-    probability p for a uniform 32-bit rnd, so that the expected value is
-    a. a >= 6 saturates to 6. The sign bit of y is kept, as in
-    ``e2m1_code``.
+    a = |y| 2^-E (exact in fp64). Below 6, with g_lo <= a < g_hi the two
+    neighbouring grid values, p = (a - g_lo) / (g_hi - g_lo) (exact: the
+    gap is 0.5, 1 or 2) and the magnitude rounds up to g_hi exactly when
+    rnd < p 2^32, i.e. with probability p for a uniform 32-bit rnd, so
+    that the expected value is a. a >= 6 saturates to 6. The sign bit of
+    y is kept, as in ``e2m1_code``.
     """
     y = np.asarray(y, dtype=np.float32)
-    E = np.asarray(E, dtype=np.int64)
-    with np.errstate(under="ignore"):
-        a = np.abs(y * np.ldexp(np.float32(1), -E).astype(np.float32)).astype(np.float64)
+    a = np.abs(np.ldexp(y.astype(np.float64), -np.asarray(E, dtype=np.int64)))
     lo = ((a >= 0.5).astype(np.int64) + (a >= 1.0) + (a >= 1.5) + (a >= 2.0) + (a >= 3.0)
           + (a >= 4.0) + (a >= 6.0))
     g_lo = E2M1_GRID[lo]

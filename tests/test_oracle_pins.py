@@ -827,3 +827,165 @@ def test_sr_is_unbiased():
     scale = np.repeat(np.ldexp(1.0, sc.astype(np.int64) - 127), 32, axis=1)
     gap = np.where(np.abs(xf) / scale < 2, 0.5, np.where(np.abs(xf) / scale < 4, 1.0, 2.0)) * scale
     assert np.all(np.abs(mean - xf) <= 6 * gap / 2 / math.sqrt(n))
+
+
+# ------------------------------------ ideal quantizer Q* ([P3] core insight)
+def _exact_ideal(block):
+    """Q*(x) of one block by exact rational arithmetic, written from [P3]'s
+    core insight: s* = max|x| / q_max, and each x maps to s* times the grid
+    value nearest x / s* (ties to the even code; nothing lies beyond q_max,
+    so the nearest value of a larger t is q_max itself). Grid and q_max are
+    the printed ones (tests/golden)."""
+    grid = [Fraction(g) for _, g in _golden_table("e2m1_grid.txt")]
+    q_max = Fraction(dict(_golden_table("format_constants.txt"))["q_max"])
+    xs = [Fraction(float(v)) for v in block]
+    m_b = max(abs(v) for v in xs)
+    if m_b == 0:
+        return [Fraction(0)] * len(xs)
+    s = m_b / q_max
+    out = []
+    for v in xs:
+        t = abs(v) / s
+        code = min(range(8), key=lambda c: (abs(t - grid[c]), c % 2))
+        out.append((s * grid[code]) * (-1 if v < 0 else 1))
+    return out
+
+
+def test_ideal_quantizer_hand_worked_blocks():
+    """Hand-worked Q* outside the deadzone ([P3] core insight).
+    m_b = 6, s* = 1: the seven ties 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 go to
+    the even code (0, 1, 1, 2, 2, 4, 4); 0.3 -> 0.5, 4.9 -> 4, -0.75 -> -1.
+    m_b = 7, s* = 7/6: 1 -> t = 6/7 -> 1, Q* = 7/6; 3.5 -> t = 3, Q* = 3.5;
+    0.5 -> t = 3/7 -> 0.5, Q* = 7/12; 7 -> 7.
+    m_b = 3, s* = 1/2: 1.25 -> t = 2.5 (tie) -> 2, Q* = 1; 0.375 -> t = 0.75
+    (tie) -> 1, Q* = 0.5; 0.1 is in the deadzone (24 * 0.1 < 3) -> 0."""
+    cases = [
+        ([6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.3, 4.9, -0.75],
+         [6, 0, 1, 1, 2, 2, 4, 4, 0.5, 4, -1]),
+        ([7, 1, 3.5, 0.5], [7, Fraction(7, 6), 3.5, Fraction(7, 12)]),
+        ([3, 1.25, 0.375, 0.1], [3, 1, 0.5, 0]),
+    ]
+    for vals, want in cases:
+        blk = np.zeros((1, 32), dtype=np.float32)
+        blk[0, :len(vals)] = vals
+        for mode in (O.MODE_OCP_FLOOR, O.MODE_CEIL):
+            d = O.error_decomposition(blk, mode)
+            for i, w in enumerate(want):
+                assert Fraction(d["Q_star"][0, i]) == pytest.approx(Fraction(w), rel=1e-15, abs=0), \
+                    (vals, i)
+    # the m_b = 3 block: 0.1 is the only deadzone element among the non-zero ones
+    blk = np.zeros((1, 32), dtype=np.float32)
+    blk[0, :4] = [3, 1.25, 0.375, 0.1]
+    d = O.error_decomposition(blk, O.MODE_CEIL)
+    assert list(d["deadzone"][0, :4]) == [False, False, False, True]
+    # m_b = 7 in floor mode: E = 0, Q(1) = 1, so e_scale = 1 - 7/6 = -1/6;
+    # Q(3.5) = 4 (tie to the even code), e_scale = 1/2; e_grid(3.5) = 0
+    blk = np.zeros((1, 32), dtype=np.float32)
+    blk[0, :4] = [7, 1, 3.5, 0.5]
+    d = O.error_decomposition(blk, O.MODE_OCP_FLOOR)
+    assert d["e_scale"][0, 1] == pytest.approx(-1 / 6, rel=1e-14)
+    assert d["e_scale"][0, 2] == 0.5 and d["e_grid"][0, 2] == 0.0
+    assert d["e_grid"][0, 3] == pytest.approx(7 / 12 - 0.5, rel=1e-14)
+
+
+def test_ideal_quantizer_against_exact_rationals():
+    """Q* of the oracle against the exact rational rule on heavy-tailed
+    blocks, plus blocks built to hold exact ties of x / s* (x = tie * m_b / 6
+    for m_b = 6 * 2^k and for m_b = 3 * 2^k)."""
+    rng = np.random.default_rng(41)
+    a = rng.standard_t(3, size=(300, 32)) * rng.lognormal(0, 1, size=(300, 1))
+    blocks = [O.bf16_to_f32(synthetic.f64_to_bf16_bits(a))]
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    for k in range(-6, 7):
+        for base in (6.0, 3.0, 4.5):
+            m_b = base * 2.0 ** k
+            t = np.zeros((1, 32), dtype=np.float32)
+            t[0, 0] = m_b
+            t[0, 1:8] = ties * m_b / 6
+            t[0, 8:15] = -ties * m_b / 6
+            t[0, 15:32] = rng.uniform(-m_b, m_b, 17)
+            blocks.append(t)
+    blocks = np.concatenate(blocks)
+    for mode in (O.MODE_OCP_FLOOR, O.MODE_CEIL):
+        d = O.error_decomposition(blocks, mode)
+        for b in range(blocks.shape[0]):
+            want = _exact_ideal(blocks[b])
+            for i in range(32):
+                got = Fraction(d["Q_star"][b, i])
+                assert abs(got - want[i]) <= abs(want[i]) * Fraction(1, 2 ** 50), (b, i)
+            dz = [24 * abs(Fraction(float(v))) < max(abs(Fraction(float(u))) for u in blocks[b])
+                  for v in blocks[b]]
+            assert list(d["deadzone"][b]) == dz
+
+
+# --------------------------------------------- GEMM tolerance and the report
+def test_gemm_tolerance_matches_the_stated_bound():
+    """gemm_tolerance is the stated bound and nothing looser: 1e-5 * S for
+    fp32 output, plus bf16's round-to-nearest step 2^-8 |C_ref| for bf16
+    output (tests/golden/format_constants.txt)."""
+    consts = dict(_golden_table("format_constants.txt"))
+    tol = float(consts["gemm_abs_sum_tol"])
+    u = 2.0 ** int(consts["bf16_roundoff_log2"])
+    S = np.array([0.0, 1.0, 3.5, 1e6])
+    c = np.array([0.0, -2.0, 0.5, 7e5])
+    assert np.array_equal(O.gemm_tolerance(S, c, False), tol * S)
+    assert np.array_equal(O.gemm_tolerance(S, c, True), tol * S + u * np.abs(c))
+
+
+def test_bf16_roundoff_constant_is_the_rounding_bound():
+    """The 2^-8 of the bf16 output term is the largest relative change that
+    rounding fp32 to bf16 (torch's round-to-nearest-even cast, a library
+    routine) makes, and it is approached: a smaller constant would reject
+    correctly rounded outputs."""
+    import torch
+    rng = np.random.default_rng(3)
+    bits = rng.integers(0x00800000, 0x7F000000, size=1 << 20, dtype=np.uint32)
+    # values just above 1 + 2^-8 * k: the worst case sits at half an ulp
+    bits[:4096] = (0x3F800000 + 0x7FFF + np.arange(4096, dtype=np.uint32) * 0x10000) & 0x7FFFFFFF
+    x = bits.view(np.float32)
+    xb = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    rel = np.abs(xb.astype(np.float64) - x) / np.abs(x.astype(np.float64))
+    u = 2.0 ** int(dict(_golden_table("format_constants.txt"))["bf16_roundoff_log2"])
+    assert rel.max() <= u
+    assert rel.max() > u * (1 - 2.0 ** -6)
+
+
+def test_error_report_closed_forms():
+    """MSE, cosine, relative Frobenius error and SNR on perturbations with
+    closed-form values: C = P (1 + eps) gives rel_fro = eps, cosine = 1,
+    SNR = -20 log10(eps); C = P + D with D orthogonal to P gives
+    cosine = |P| / sqrt(|P|^2 + |D|^2) and MSE = |D|^2 / n."""
+    rng = np.random.default_rng(5)
+    P = rng.standard_normal((16, 24))
+    r = O.error_report(P * 1.125, P)
+    assert r["rel_fro"] == pytest.approx(0.125, rel=1e-12)
+    assert r["cosine"] == pytest.approx(1.0, rel=1e-12)
+    assert r["snr_db"] == pytest.approx(-20 * math.log10(0.125), rel=1e-12)
+    D = rng.standard_normal(P.shape)
+    D -= P * np.sum(D * P) / np.sum(P * P)
+    r = O.error_report(P + D, P)
+    nP, nD = np.sum(P * P), np.sum(D * D)
+    assert r["cosine"] == pytest.approx(math.sqrt(nP / (nP + nD)), rel=1e-10)
+    assert r["mse"] == pytest.approx(nD / P.size, rel=1e-12)
+    assert r["snr_db"] == pytest.approx(10 * math.log10(nP / nD), rel=1e-12)
+
+
+def test_sr_scaled_value_below_the_fp32_range():
+    """A scaled value far below fp32's range still has p > 0 in the exact
+    definition, so rand = 0 rounds it up to 0.5 and rand = 1 does not.
+    Block {2^19, 2^-133, 0...}, no rotation: E = 17 in both rules, and the
+    bf16 subnormal 2^-133 scales to 2^-150, which an fp32 multiply would
+    round to 0."""
+    row = np.zeros((1, 32), dtype=np.uint16)
+    row[0, 0] = synthetic.f64_to_bf16_bits(np.array([2.0 ** 19]))[0]
+    row[0, 1] = 0x0001            # 2^-133, the smallest bf16 subnormal
+    row[0, 2] = 0x8001            # -2^-133
+    assert synthetic.bf16_bits_to_f32(row)[0, 1] == 2.0 ** -133
+    for mode in (O.MODE_OCP_FLOOR, O.MODE_CEIL):
+        for r, want in ((0, 1), (1, 0)):
+            rnd = np.full((1, 32), r, np.uint32)
+            nib, sc = O.quantize_sr(row, O.AXIS_ROW, 0, mode, rnd)
+            assert sc[0, 0] == 127 + 17
+            codes = _codes_of(nib)[0]
+            assert codes[1] == want and codes[2] == 8 | want
+            assert np.all(codes[3:] == 0)
