@@ -104,11 +104,21 @@ def cpu_baseline(work, budget_rows=2048, budget_cols=8192):
     (quantize the matching source slices, dequantize, fp64 GEMM + sum|a||b|)."""
     import numpy as np
     import oracle as O
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
-        cores = 1
+        blas = None
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     flops = qbytes = tq = 0.0
     t0 = time.perf_counter()
     for name, wl, op, (T, N, K), (pn, qn) in PRODUCTS:
@@ -116,27 +126,29 @@ def cpu_baseline(work, budget_rows=2048, budget_cols=8192):
         (_, _), (_, _), (GM, GN, GK) = plan(op, T, N, K)
         m, n = min(budget_rows, GM), min(budget_cols, GN)
         tq0 = time.perf_counter()
+        def q(src, axis):
+            return O.quantize_chunked(np.ascontiguousarray(src), axis, 16, 0, chunk=64,
+                                      threads=cores)
         if op == "fprop":
-            qa = O.quantize(P[:m], O.AXIS_ROW, 16, 0)
-            qb = O.quantize(Q[:n], O.AXIS_ROW, 16, 0)
+            qa, qb = q(P[:m], O.AXIS_ROW), q(Q[:n], O.AXIS_ROW)
         elif op == "dgrad":
-            qa = O.quantize(P[:m], O.AXIS_ROW, 16, 0)
-            qb = O.quantize(np.ascontiguousarray(Q[:, :n]), O.AXIS_COL, 16, 0)
+            qa, qb = q(P[:m], O.AXIS_ROW), q(Q[:, :n], O.AXIS_COL)
         else:
-            qa = O.quantize(np.ascontiguousarray(P[:, :m]), O.AXIS_COL, 16, 0)
-            qb = O.quantize(np.ascontiguousarray(Q[:, :n]), O.AXIS_COL, 16, 0)
+            qa, qb = q(P[:, :m], O.AXIS_COL), q(Q[:, :n], O.AXIS_COL)
         tq += time.perf_counter() - tq0
         qbytes += (m + n) * GK * (2 + 0.5 + 1 / 32)
         O.gemm_ref(O.dequantize(*qa), O.dequantize(*qb))
         flops += 2.0 * m * n * GK
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": model, "blas_threads": blas,
             "seconds": round(dt, 3),
             "quantize_GB/s": round(qbytes / tq / 1e9, 3),
             "gemm_GFLOP/s": round(flops / (dt - tq) / 1e9, 1),
             "sample": f"{budget_rows}x{budget_cols} output tile of each of the 4 products at full "
-                      f"reduction length: oracle rotate+quantize of the matching source slices, "
-                      f"dequantize, fp64 GEMM and sum|a||b| (numpy; BLAS threads = {cores})"}
+                      f"reduction length: oracle rotate+quantize of the matching source slices "
+                      f"({cores} threads over 64-row or 64-column slabs), dequantize, fp64 GEMM "
+                      f"and sum|a||b| (numpy; BLAS threads = {blas})"}
 
 
 def gemm_error(mx, an, asc, bn, bsc, p, ref, rows, stream):

@@ -207,19 +207,25 @@ def quantize(src_bf16: np.ndarray, axis: int, hadamard: int, mode: int):
 
 
 def quantize_chunked(src_bf16: np.ndarray, axis: int, hadamard: int, mode: int,
-                     chunk: int = 1024):
+                     chunk: int = 1024, threads: int = 1):
     """``quantize`` over row (or, for col, column) slabs to bound memory.
 
     Blocks never straddle slabs (slab sizes are multiples of 32), so the
-    result equals ``quantize`` on the whole matrix.
+    result equals ``quantize`` on the whole matrix. With ``threads`` > 1 the
+    slabs are quantized by a thread pool (numpy's array operations release
+    the interpreter lock); the slabs and their order are the same.
     """
     r, c = src_bf16.shape
     if axis == AXIS_COL:
-        parts = [quantize(src_bf16[:, j:j + chunk], axis, hadamard, mode)
-                 for j in range(0, c, chunk)]
+        slabs = [src_bf16[:, j:j + chunk] for j in range(0, c, chunk)]
     else:
-        parts = [quantize(src_bf16[i:i + chunk], axis, hadamard, mode)
-                 for i in range(0, r, chunk)]
+        slabs = [src_bf16[i:i + chunk] for i in range(0, r, chunk)]
+    if threads > 1 and len(slabs) > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            parts = list(ex.map(lambda s: quantize(s, axis, hadamard, mode), slabs))
+    else:
+        parts = [quantize(s, axis, hadamard, mode) for s in slabs]
     return (np.concatenate([p[0] for p in parts], axis=0),
             np.concatenate([p[1] for p in parts], axis=0))
 

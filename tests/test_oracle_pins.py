@@ -989,3 +989,14 @@ def test_sr_scaled_value_below_the_fp32_range():
             codes = _codes_of(nib)[0]
             assert codes[1] == want and codes[2] == 8 | want
             assert np.all(codes[3:] == 0)
+
+
+@pytest.mark.parametrize("axis", [O.AXIS_ROW, O.AXIS_COL])
+def test_threaded_slabs_equal_the_whole_matrix(axis):
+    """The thread-pool form of the slab quantizer (the CPU baseline's) gives
+    the bytes of one call on the whole matrix."""
+    x = synthetic.f64_to_bf16_bits(np.random.default_rng(17).standard_t(3, size=(160, 224)))
+    whole = O.quantize(x, axis, 16, O.MODE_OCP_FLOOR)
+    for chunk, threads in ((32, 4), (64, 8), (1, 3)):
+        got = O.quantize_chunked(x, axis, 16, O.MODE_OCP_FLOOR, chunk=chunk, threads=threads)
+        assert np.array_equal(got[0], whole[0]) and np.array_equal(got[1], whole[1])
