@@ -1051,12 +1051,17 @@ __global__ __launch_bounds__(256) void quant_rs_row_kernel(const uint4* __restri
 
 // Stochastic rounding (SR) of one rotated value y in a finite block with
 // E8M0 byte s (E = s - 127), with one uniform 32-bit integer u:
-// a = |fl32(y 2^-E)|; below 6, between the neighbouring grid values
+// a = |y| 2^-E; below 6, between the neighbouring grid values
 // g_lo <= a < g_hi, round up exactly when u < p 2^32 with
 // p = (a - g_lo) / (g_hi - g_lo), i.e. with probability p; a >= 6 gives 6.
-// All in fp32 and exact: a - g_lo is exact (g_lo = 0, or g_hi <= 2 g_lo),
-// the gap is 0.5, 1 or 2, and for an fp32 p < 1 the threshold
-// t = p 2^32 <= 2^32 - 2^8, so u < t is u < ceil(t) as integers.
+// In fp32 and exact: the multiply by 2^-E is exact unless its result falls
+// below 2^-126 with bits lost, a - g_lo is exact (g_lo = 0, or
+// g_hi <= 2 g_lo), the gap is 0.5, 1 or 2, and for an fp32 p < 1 the
+// threshold t = p 2^32 <= 2^32 - 2^8, so u < t is u < ceil(t) as integers.
+// Where the multiply loses bits, the exact threshold 2^33 a is below 2^-93:
+// only u = 0 rounds up, and it does whenever y != 0, which the limit of at
+// least 1 for a non-zero y in the lowest interval gives also when the
+// product rounds to 0.
 // Returns the 4-bit code (sign of y kept).
 __device__ __forceinline__ uint32_t sr_code(float y, uint32_t s, uint32_t u) {
   const float inv = s == 254u ? __uint_as_float(0x00400000u) : __uint_as_float((254u - s) << 23);
@@ -1066,7 +1071,8 @@ __device__ __forceinline__ uint32_t sr_code(float y, uint32_t s, uint32_t u) {
   const float glo = lo < 4 ? 0.5f * (float)lo : (lo == 4 ? 2.0f : (lo == 5 ? 3.0f : 4.0f));
   const float k = lo < 4 ? 8589934592.0f : (lo < 6 ? 4294967296.0f : 2147483648.0f);
   const float t = lo >= 7 ? 0.0f : (a - glo) * k;
-  const uint32_t lim = (uint32_t)ceilf(t);
+  const uint32_t nz = (lo == 0 && (__float_as_uint(y) & 0x7FFFFFFFu) != 0u) ? 1u : 0u;
+  const uint32_t lim = max((uint32_t)ceilf(t), nz);
   const uint32_t mag = lo >= 7 ? 7u : (uint32_t)lo + (u < lim ? 1u : 0u);
   return mag | ((__float_as_uint(y) >> 28) & 8u);
 }

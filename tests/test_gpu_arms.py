@@ -121,3 +121,31 @@ def test_arms_workload_full_size(quant_workload, axis):
     rnd = synthetic.random_u32(a.shape, 42)
     assert_same(gpu_sr(a, axis, 16, 0, rnd), O.quantize_sr(a, axis, 16, 0, rnd),
                 f"sr full axis={axis}")
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+def test_sr_scaled_values_below_fp32_range_on_gpu(axis):
+    """Blocks whose large first element puts E at 8..27 while the other
+    rotation group holds bf16 subnormals: the scaled values fall below
+    2^-149, where an fp32 multiply rounds to 0 but the exact p is positive,
+    so u = 0 must round them up to 0.5. Random u elsewhere, both rules,
+    H0/H16/H32 (H32 mixes the groups, which the oracle follows as well)."""
+    rng = np.random.default_rng(77)
+    R = 64
+    bits = np.zeros((R, 64), np.uint16)
+    for r in range(R):
+        bits[r, 0] = synthetic.f64_to_bf16_bits(np.array([2.0 ** (10 + r % 20)]))[0]
+        bits[r, 16:32] = rng.integers(1, 0x80, 16) | (rng.integers(0, 2, 16) << 15)
+        bits[r, 32] = bits[r, 0]
+        bits[r, 48:64] = rng.integers(1, 0x80, 16)
+    if axis == 1:
+        bits = np.ascontiguousarray(bits.T)
+    for mode in (0, 1):
+        for h in (0, 16, 32):
+            rnd = synthetic.random_u32(bits.shape, 78)
+            rnd[rng.random(bits.shape) < 0.5] = 0
+            assert_same(gpu_sr(bits, axis, h, mode, rnd), O.quantize_sr(bits, axis, h, mode, rnd),
+                        f"sr underflow axis={axis} h={h} mode={mode}")
+            want = O.quantize_sr(bits, axis, h, mode, np.zeros(bits.shape, np.uint32))
+            assert_same(gpu_sr(bits, axis, h, mode, np.zeros(bits.shape, np.uint32)), want,
+                        f"sr underflow u=0 axis={axis} h={h} mode={mode}")

@@ -62,6 +62,11 @@ SHAPES = [
     (300, 520, 6144),    # LDS-DMA kernel, ragged M and N, three scale-group pairs
     (257, 261, 2048),    # LDS-DMA kernel, N % 4 != 0 (element-wise epilogue)
     (513, 260, 8192),    # LDS-DMA kernel, the Wgrad reduction length
+    # more 256x256 tiles than the GPU has compute units, with ragged last
+    # tiles: later tiles of each work-group start from operands that the
+    # previous tile's k-loop prefetched
+    (6448, 6504, 2048),  # 26 x 26 = 676 tiles, both edges ragged
+    (4200, 4400, 4096),  # 17 x 18 = 306 tiles, the Llama reduction length
 ]
 
 

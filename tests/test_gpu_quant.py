@@ -189,3 +189,41 @@ def test_dual_edge_values_bit_exact(h, mode):
 @pytest.mark.parametrize("h,mode", [(16, 0), (16, 1), (32, 0), (0, 1)])
 def test_dual_quantizer_workload_full_size(quant_workload, h, mode):
     assert_dual_same(quant_workload, h, mode, f"dual full h={h} mode={mode}")
+
+
+def exhaustive_encode_matrix(mode):
+    """Every finite bf16 value, both signs, at every shared exponent E the
+    format reaches: for each bf16 exponent field f = 0..254 one anchor
+    (element 0 of its blocks) fixes E -- mantissa 1.1111111b in OCP floor
+    mode (so scaled values reach 7.97 and the saturation band), mantissa
+    1.1b in ceil mode (scaled values reach 6 exactly) -- and the other 31
+    elements of those blocks run through every finite bf16 value of
+    magnitude at most the anchor. H0 row blocks, 32 blocks per row."""
+    mags = np.arange(0x7F80, dtype=np.uint16)          # +0 .. bf16 max
+    anchors_m = 0x7F if mode == 0 else 0x40
+    blocks = []
+    for f in range(255):
+        anchor = np.uint16((f << 7) | anchors_m)
+        vals = mags[mags <= anchor]
+        vals = np.concatenate([vals, vals | 0x8000])   # both signs
+        n = -(-vals.size // 31)
+        body = np.zeros(n * 31, np.uint16)
+        body[:vals.size] = vals
+        blk = np.empty((n, 32), np.uint16)
+        blk[:, 0] = anchor
+        blk[:, 1:] = body.reshape(n, 31)
+        blocks.append(blk)
+    b = np.concatenate(blocks)
+    pad = (-b.shape[0]) % 32
+    b = np.concatenate([b, np.zeros((pad, 32), np.uint16)])
+    return b.reshape(-1, 1024)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_e2m1_encode_exhaustive(mode):
+    """The hardware's scaled FP4 convert against the oracle's nearest-value
+    rule ([P1] section A.1: round to the nearest FP4 value) over every
+    finite bf16 value at every shared exponent, row-wise and column-wise."""
+    bits = exhaustive_encode_matrix(mode)
+    assert_same(bits, 0, 0, mode, f"exhaustive encode row mode={mode}")
+    assert_same(np.ascontiguousarray(bits.T), 1, 0, mode, f"exhaustive encode col mode={mode}")
