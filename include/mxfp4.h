@@ -242,6 +242,28 @@ int mxfp4_error_stats(const void* src_bf16, int64_t rows, int64_t cols, int axis
                       double* out_stats, hipStream_t stream);
 
 /*
+ * mxfp4_error_stats_noalloc -- mxfp4_error_stats without a workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, results and errors as mxfp4_error_stats minus ws and
+ * ws_bytes; out_stats (DEVICE, 10 doubles, 8-byte aligned) is still the
+ * caller's. The per-work-group partial sums go to a static device array of
+ * the library, 1024 x 10 doubles (80 KiB), that every GPU the library runs
+ * on holds until the process ends. Any input size fits: the first pass
+ * never launches more than 1024 work-groups. Allocates nothing and calls no
+ * allocating routine; the array's device address is looked up on the first
+ * call on each device (with that device current), so `stream` must belong
+ * to the current device. Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (concurrent streams, or threads) race and
+ * give wrong sums; calls ordered on one stream are safe. Nothing needs
+ * clearing: each call writes every partial it reads.
+ */
+int mxfp4_error_stats_noalloc(const void* src_bf16, int64_t rows, int64_t cols, int axis,
+                              int hadamard, int scale_mode, double* out_stats,
+                              hipStream_t stream);
+
+/*
  * mxfp4_gemm -- C[M][N] = sum_k deqA[m][k] * deqB[n][k] on gfx950's
  * block-scaled FP4 MFMA with FP32 accumulation ([P1] A.2; [P3]).
  *

@@ -29,7 +29,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp4.so
 
 EXPORTS = (
     "mxfp4_quantize", "mxfp4_quantize_dual", "mxfp4_quantize_of", "mxfp4_quantize_mbs",
-    "mxfp4_quantize_rs", "mxfp4_quantize_sr", "mxfp4_error_stats", "mxfp4_gemm", "mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad",
+    "mxfp4_quantize_rs", "mxfp4_quantize_sr", "mxfp4_error_stats",
+    "mxfp4_error_stats_noalloc", "mxfp4_gemm", "mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad",
     "mxfp4_workspace_bytes", "mxfp4_status_string",
 )
 
@@ -66,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mxfp4_quantize_sr.restype = i32
     lib.mxfp4_error_stats.argtypes = [p, i64, i64, i32, i32, i32, p, sz, p, p]
     lib.mxfp4_error_stats.restype = i32
+    lib.mxfp4_error_stats_noalloc.argtypes = [p, i64, i64, i32, i32, i32, p, p]
+    lib.mxfp4_error_stats_noalloc.restype = i32
     lib.mxfp4_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
     lib.mxfp4_gemm.restype = i32
     for name in ("mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad"):
@@ -208,6 +211,19 @@ def mxfp4_error_stats(src, rows, cols, axis, hadamard, scale_mode, ws, out_stats
     _check(load_library().mxfp4_error_stats(_ptr(src), rows, cols, axis, hadamard, scale_mode,
                                             _ptr(ws), ws.numel(), _ptr(out_stats),
                                             _stream(stream)), "mxfp4_error_stats")
+
+
+def mxfp4_error_stats_noalloc(src, rows, cols, axis, hadamard, scale_mode, out_stats,
+                              stream=None):
+    """mxfp4_error_stats with the library's static partial-sum array
+    instead of a workspace (allocates nothing)."""
+    import torch
+    _need(src, torch.bfloat16, rows * cols, "src")
+    _need(out_stats, torch.float64, ERROR_STATS_COUNT, "out_stats")
+    _check(load_library().mxfp4_error_stats_noalloc(_ptr(src), rows, cols, axis, hadamard,
+                                                    scale_mode, _ptr(out_stats),
+                                                    _stream(stream)),
+           "mxfp4_error_stats_noalloc")
 
 
 def mxfp4_gemm(Aq, As, Bq, Bs, M, N, K, C, out_dtype=OUT_F32, stream=None):

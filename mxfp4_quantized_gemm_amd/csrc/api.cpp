@@ -34,8 +34,9 @@ bool dims_ok(int64_t a, int64_t b) {
   return a >= 0 && b >= 0 && a < kMaxDim && b < kMaxDim && (a == 0 || b <= kMaxElems / a);
 }
 
-int check_quantize(const void* src, int64_t rows, int64_t cols, int axis, int hadamard,
-                   int scale_mode, const void* nib, const void* sc) {
+// Modes, shape and the bf16 source of a rotate + quantize pass.
+int check_source(const void* src, int64_t rows, int64_t cols, int axis, int hadamard,
+                 int scale_mode) {
   if (axis < MXFP4_AXIS_ROW || axis > MXFP4_AXIS_2D32 || !valid_hadamard(hadamard) ||
       !valid_mode(scale_mode))
     return MXFP4_ERR_MODE;
@@ -44,8 +45,17 @@ int check_quantize(const void* src, int64_t rows, int64_t cols, int axis, int ha
   if (blocked % 32) return MXFP4_ERR_SHAPE;
   if (axis == MXFP4_AXIS_2D32 && rows % 32) return MXFP4_ERR_SHAPE;
   if (rows == 0 || cols == 0) return MXFP4_OK;
-  if (!src || !nib || !sc) return MXFP4_ERR_NULL;
-  if (!aligned16(src) || !aligned16(nib)) return MXFP4_ERR_ALIGN;
+  if (!src) return MXFP4_ERR_NULL;
+  if (!aligned16(src)) return MXFP4_ERR_ALIGN;
+  return MXFP4_OK;
+}
+
+int check_quantize(const void* src, int64_t rows, int64_t cols, int axis, int hadamard,
+                   int scale_mode, const void* nib, const void* sc) {
+  const int st = check_source(src, rows, cols, axis, hadamard, scale_mode);
+  if (st != MXFP4_OK || rows == 0 || cols == 0) return st;
+  if (!nib || !sc) return MXFP4_ERR_NULL;
+  if (!aligned16(nib)) return MXFP4_ERR_ALIGN;
   return MXFP4_OK;
 }
 
@@ -218,6 +228,18 @@ int mxfp4_error_stats(const void* src_bf16, int64_t rows, int64_t cols, int axis
     return MXFP4_ERR_ALIGN;
   return hip_status(mx::launch_error_stats(src_bf16, rows, cols, axis, hadamard, scale_mode, ws,
                                            out_stats, stream));
+}
+
+int mxfp4_error_stats_noalloc(const void* src_bf16, int64_t rows, int64_t cols, int axis,
+                              int hadamard, int scale_mode, double* out_stats,
+                              hipStream_t stream) {
+  if (axis != MXFP4_AXIS_ROW && axis != MXFP4_AXIS_COL) return MXFP4_ERR_MODE;
+  const int st = check_source(src_bf16, rows, cols, axis, hadamard, scale_mode);
+  if (st != MXFP4_OK) return st;
+  if (!out_stats) return MXFP4_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(out_stats) & 7u) return MXFP4_ERR_ALIGN;
+  return hip_status(mx::launch_error_stats_noalloc(src_bf16, rows, cols, axis, hadamard,
+                                                   scale_mode, out_stats, stream));
 }
 
 int mxfp4_gemm(const void* Aq, const void* As, const void* Bq, const void* Bs, int64_t M,

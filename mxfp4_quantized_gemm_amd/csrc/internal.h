@@ -45,6 +45,12 @@ hipError_t launch_error_stats(const void* src, int64_t rows, int64_t cols, int a
                               int hadamard, int scale_mode, void* ws, void* out,
                               hipStream_t stream);
 
+// The same sums with the partials in a static device array of
+// kStatsMaxGroups x 10 doubles per GPU (no workspace, no allocation).
+hipError_t launch_error_stats_noalloc(const void* src, int64_t rows, int64_t cols, int axis,
+                                      int hadamard, int scale_mode, void* out,
+                                      hipStream_t stream);
+
 // Block-scaled MXFP4 GEMM, C[M][N] = A[M][K] B[N][K]^T.
 hipError_t launch_gemm(const void* Aq, const void* As, const void* Bq, const void* Bs,
                        int64_t M, int64_t N, int64_t K, void* C, int out_dtype,

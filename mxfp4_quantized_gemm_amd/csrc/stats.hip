@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "internal.h"
 #include "mxfp4_device.h"
 
@@ -211,7 +213,46 @@ hipError_t dispatch_stats_mode(const void* src, int64_t rows, int64_t cols, int 
                        : dispatch_stats<H, kOcpFloor>(src, rows, cols, axis, part, out, st);
 }
 
+// Partial sums of mxfp4_error_stats_noalloc: one row of kStats doubles per
+// work-group of the first pass, whose grid never exceeds kStatsMaxGroups.
+// Every GPU holds its own copy for the life of the process. Host code never
+// uses this name as an address (on the host it is only a stand-in for the
+// symbol): it looks the device address up once per device.
+static __device__ __align__(256) double scratch[kStatsMaxGroups * kStats];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+double* g_scratch[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on the first
+// call on that device and kept.
+hipError_t scratch_of_current_device(double** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch[dev] = static_cast<double*>(p);
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
 }  // namespace
+
+hipError_t launch_error_stats_noalloc(const void* src, int64_t rows, int64_t cols, int axis,
+                                      int hadamard, int scale_mode, void* out,
+                                      hipStream_t stream) {
+  double* part = nullptr;
+  const hipError_t e = scratch_of_current_device(&part);
+  if (e != hipSuccess) return e;
+  return launch_error_stats(src, rows, cols, axis, hadamard, scale_mode, part, out, stream);
+}
 
 hipError_t launch_error_stats(const void* src, int64_t rows, int64_t cols, int axis,
                               int hadamard, int scale_mode, void* ws, void* out,

@@ -93,6 +93,21 @@ void quantize_cases() {
   CHECK(mxfp4_error_stats(src, 64, 64, 1, 16, 0, at(32768), MXFP4_ERROR_STATS_WS_BYTES, out,
                           nullptr) == MXFP4_OK);
   CHECK(stub::g_ncalls == 1 && stub::g_calls[0].out[1] == out);
+  // the variant without a workspace: same checks on the source, out_stats
+  // 8-byte aligned, no workspace argument
+  stub::reset(hipSuccess);
+  CHECK(mxfp4_error_stats_noalloc(src, 64, 64, 2, 16, 0, out, nullptr) == MXFP4_ERR_MODE);
+  CHECK(mxfp4_error_stats_noalloc(src, 64, 48, 0, 16, 0, out, nullptr) == MXFP4_ERR_SHAPE);
+  CHECK(mxfp4_error_stats_noalloc(src, 64, 64, 0, 16, 0, nullptr, nullptr) == MXFP4_ERR_NULL);
+  CHECK(mxfp4_error_stats_noalloc(nullptr, 64, 64, 0, 16, 0, out, nullptr) == MXFP4_ERR_NULL);
+  CHECK(mxfp4_error_stats_noalloc(src, 64, 64, 0, 16, 0, reinterpret_cast<double*>(at(24580)),
+                                  nullptr) == MXFP4_ERR_ALIGN);
+  CHECK(stub::g_ncalls == 0);
+  CHECK(mxfp4_error_stats_noalloc(nullptr, 0, 64, 0, 16, 0, reinterpret_cast<double*>(at(24584)),
+                                  nullptr) == MXFP4_OK);
+  CHECK(mxfp4_error_stats_noalloc(src, 32, 64, 1, 32, 1, out, nullptr) == MXFP4_OK);
+  CHECK(stub::g_ncalls == 2 && strcmp(stub::g_calls[1].what, "stats_noalloc") == 0);
+  CHECK(stub::g_calls[1].out[0] == out && stub::g_calls[1].i[1] == 32);
 }
 
 void gemm_cases() {

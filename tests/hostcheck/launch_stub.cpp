@@ -69,6 +69,12 @@ hipError_t launch_error_stats(const void* src, int64_t rows, int64_t cols, int a
                       nullptr);
 }
 
+hipError_t launch_error_stats_noalloc(const void* src, int64_t rows, int64_t cols, int axis,
+                                      int hadamard, int scale_mode, void* out, hipStream_t) {
+  return stub::record("stats_noalloc", src, rows, cols, axis, hadamard, scale_mode, out, nullptr,
+                      nullptr, nullptr);
+}
+
 hipError_t launch_gemm(const void* Aq, const void* As, const void* Bq, const void* Bs, int64_t M,
                        int64_t N, int64_t K, void* C, int out_dtype, hipStream_t) {
   const hipError_t r = stub::record("gemm", Aq, M, N, out_dtype, 0, 0, const_cast<void*>(As),
