@@ -230,6 +230,33 @@ def error_report(mx, torch, prods, stream, dev, rows=128):
                 rec[f"sr_h16_{['ocp_floor', 'ceil'][m]}"] = gemm_error(
                     mx, an, asc, bn, bsc, p, ref, rows, stream)
                 del an, asc, bn, bsc, ra, rb
+                # macro-block scaling ([P3] MBS: prescale, quantize, postscale)
+                # on both operands, multiplied by the MBS GEMM
+                qa = mx.quantize_mbs(p["P"], mx.AXIS_ROW, 16, m, stream)
+                qb = mx.quantize_mbs(p["Q"], mx.AXIS_ROW, 16, m, stream)
+                args = (*qa, *qb, p["GM"], p["GN"], p["GK"], p["C"], mx.OUT_F32, stream)
+                mx.mxfp4_gemm_mbs(*args)
+                c = p["C"][:rows].double()
+                d = c - ref
+                nd, nr = float((d * d).sum()), float((ref * ref).sum())
+                key = f"mbs_h16_{['ocp_floor', 'ceil'][m]}"
+                rec[key] = {"mse": float((d * d).mean()),
+                            "cosine": float((c * ref).sum() / (c.norm() * ref.norm())),
+                            "rel_fro": (nd / nr) ** 0.5,
+                            "snr_db": 10.0 * np.log10(nr / nd)}
+                if m == 1:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for _ in range(10):
+                        mx.mxfp4_gemm_mbs(*args)
+                    e1.record(stream)
+                    e1.synchronize()
+                    us = e0.elapsed_time(e1) / 10 * 1e3
+                    rec["mbs_gemm_us"] = round(us, 2)
+                    rec["mbs_gemm_TFLOPs"] = round(
+                        2.0 * p["GM"] * p["GN"] * p["GK"] / (us * 1e-6) / 1e12, 1)
+                del qa, qb, args
         out[p["name"]] = rec
         del ref
     torch.cuda.synchronize()
@@ -369,12 +396,13 @@ def main():
                            device=dev),
         ))
 
-    def launches(p):
+    def launches(p, mode=0):
+        # both operands in one launch (mxfp4_quantize_pair), then the GEMM:
+        # the launches mxfp4_fprop / dgrad / wgrad issue
         return [
-            lambda: mx.mxfp4_quantize(p["P"], p["sa"][0], p["sa"][1], p["axa"], 16, 0, p["an"],
-                                      p["asc"], stream),
-            lambda: mx.mxfp4_quantize(p["Q"], p["sb"][0], p["sb"][1], p["axb"], 16, 0, p["bn"],
-                                      p["bsc"], stream),
+            lambda: mx.mxfp4_quantize_pair(p["P"], p["sa"][0], p["sa"][1], p["axa"], p["an"],
+                                           p["asc"], p["Q"], p["sb"][0], p["sb"][1], p["axb"],
+                                           p["bn"], p["bsc"], 16, mode, stream),
             lambda: mx.mxfp4_gemm(p["an"], p["asc"], p["bn"], p["bsc"], p["GM"], p["GN"], p["GK"],
                                   p["C"], mx.OUT_F32, stream),
         ]
@@ -404,6 +432,19 @@ def main():
     total_flops = sum(2.0 * p["GM"] * p["GN"] * p["GK"] for p in prods)
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
+    # the same step with ceiling-rounded scales (the rule that keeps the
+    # heavy-tailed Wgrad operand from clipping; same kernels otherwise)
+    seq_ceil = [fn for p in prods for fn in launches(p, 1)]
+    for fn in seq_ceil:
+        fn()
+    torch.cuda.synchronize()
+    t_c = time.perf_counter()
+    for s in range(K_):
+        for fn in seq_ceil:
+            fn()
+    torch.cuda.synchronize()
+    ceil_ms_per_step = (time.perf_counter() - t_c) * 1e3 / K_
+
     # ------------------------------------- per-kernel pass (events per launch)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)] for _ in range(K_)]
     for s in range(K_):
@@ -422,13 +463,14 @@ def main():
     for idx, (p, j, _) in enumerate(seq):
         name = p["name"]
         rec = per_product.setdefault(name, {"GEMM_MNK": [p["GM"], p["GN"], p["GK"]]})
-        if j < 2:
-            shape, axis = (p["sa"], p["axa"]) if j == 0 else (p["sb"], p["axb"])
-            b = quant_bytes(shape[0], shape[1], axis)
+        if j == 0:
+            b = (quant_bytes(p["sa"][0], p["sa"][1], p["axa"]) +
+                 quant_bytes(p["sb"][0], p["sb"][1], p["axb"]))
             gbs = b / (kernel_ms[idx] * 1e-3) / 1e9
-            rec["quant_" + "AB"[j] + "_us"] = round(kernel_ms[idx] * 1e3, 2)
-            rec["quant_" + "AB"[j] + "_GBs"] = round(gbs, 1)
-            kernels.append({"kernel": f"{name}.quant_{'AB'[j]}", "axis": ["row", "col", "2d"][axis],
+            rec["quant_AB_us"] = round(kernel_ms[idx] * 1e3, 2)
+            rec["quant_AB_GBs"] = round(gbs, 1)
+            kernels.append({"kernel": f"{name}.quant_AB",
+                            "axes": [["row", "col"][p["axa"]], ["row", "col"][p["axb"]]],
                             "us": round(kernel_ms[idx] * 1e3, 2),
                             "us_median": round(kernel_med[idx] * 1e3, 2),
                             "us_min": round(kernel_min[idx] * 1e3, 2), "GB/s": round(gbs, 1),
@@ -438,7 +480,7 @@ def main():
             tf = f / (kernel_ms[idx] * 1e-3) / 1e12
             rec["gemm_us"] = round(kernel_ms[idx] * 1e3, 2)
             rec["gemm_TFLOPs"] = round(tf, 1)
-            tot = kernel_ms[idx - 2] + kernel_ms[idx - 1] + kernel_ms[idx]
+            tot = kernel_ms[idx - 1] + kernel_ms[idx]
             rec["fused_TFLOPs"] = round(f / (tot * 1e-3) / 1e12, 1)
             kernels.append({"kernel": f"{name}.gemm", "us": round(kernel_ms[idx] * 1e3, 2),
                             "us_median": round(kernel_med[idx] * 1e3, 2),
@@ -688,6 +730,8 @@ def main():
                    "parallelism": "single-gpu"},
         "event_ms_per_step": round(event_ms_per_step, 4),
         "fused_entry_ms_per_step": round(fused_ms, 4),
+        "ceil_scales_ms_per_step": round(ceil_ms_per_step, 4),
+        "ceil_scales_TFLOP/s": round(total_flops / (ceil_ms_per_step * 1e-3) / 1e12, 2),
         "products": per_product,
         "kernels": kernels,
         "quantizer": quant,

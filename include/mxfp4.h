@@ -105,6 +105,24 @@ int mxfp4_quantize(const void* src_bf16, int64_t rows, int64_t cols, int axis,
                    hipStream_t stream);
 
 /*
+ * mxfp4_quantize_pair -- the two operands of a product in one call: the
+ * outputs of mxfp4_quantize(src_a, rows_a, cols_a, axis_a, ...) and
+ * mxfp4_quantize(src_b, ...) with the same hadamard and scale_mode, byte
+ * for byte. Where both shapes allow it (row-wise operands; column-wise
+ * operands with rows % 256 == 0, cols % 4 == 0 and e8m0 8-byte aligned)
+ * both run in ONE launch over the two grids, which saves one launch's ramp
+ * and tail ([P1] Table 2 note: memory bandwidth is the bottleneck of these
+ * steps); otherwise two launches. Axes ROW or COL (2D32 returns
+ * MXFP4_ERR_MODE); each operand validated as by mxfp4_quantize, errors of
+ * operand A first; an empty operand launches nothing. The outputs must not
+ * overlap each other or the sources.
+ */
+int mxfp4_quantize_pair(const void* src_a, int64_t rows_a, int64_t cols_a, int axis_a,
+                        void* nibbles_a, void* e8m0_a, const void* src_b, int64_t rows_b,
+                        int64_t cols_b, int axis_b, void* nibbles_b, void* e8m0_b, int hadamard,
+                        int scale_mode, hipStream_t stream);
+
+/*
  * mxfp4_quantize_dual -- one read of src[rows][cols], both orientations.
  * ([P1] A.2 and D: the activation X feeds Fprop rotated and blocked along
  * its feature axis and Wgrad rotated and blocked along the token axis;
@@ -159,7 +177,7 @@ int mxfp4_quantize_of(const void* src_bf16, int64_t rows, int64_t cols, int axis
  * exactly mxfp4_quantize's output for fl32(c y); out_mbs receives m,
  * [rows][cols/128] (ROW) or [cols][rows/128] (COL). The value is
  * dequant(nibbles, e8m0) / c; a GEMM consuming it needs that per-128-k
- * factor on each operand (not provided by mxfp4_gemm). The blocked axis
+ * factor on each operand (mxfp4_gemm_mbs; not mxfp4_gemm). The blocked axis
  * must be a multiple of 128; otherwise as mxfp4_quantize (axis 2D32 returns
  * MXFP4_ERR_MODE).
  */
@@ -279,11 +297,29 @@ int mxfp4_gemm(const void* Aq, const void* As, const void* Bq, const void* Bs,
                hipStream_t stream);
 
 /*
+ * mxfp4_gemm_mbs -- the product of two macro-block-scaled operands
+ * (mxfp4_quantize_mbs outputs; [P3] "three targeted fixes" section, MBS:
+ * prescale by c = 1 + m/256, quantize, postscale by 1/c per 128-element
+ * macro-block):
+ *   C[m][n] = sum_k (deqA[m][k] / cA[m][k/128]) (deqB[n][k] / cB[n][k/128]).
+ * A: Aq [M][K/2], As [M][K/32], Am [M][K/128] mantissa bytes; B likewise
+ * with N rows; all K-contiguous. Each 128-k macro-block's MXFP4 product is
+ * accumulated in fp32 and added to C times fl32(1/cA) fl32(1/cB) (FP32
+ * accumulation as in mxfp4_gemm). C: as mxfp4_gemm (fp32 or bf16,
+ * overwritten). M >= 1, N >= 1, K >= 128, K % 128 == 0; other errors as
+ * mxfp4_gemm (Am and Bm may have any alignment). One launch on `stream`.
+ */
+int mxfp4_gemm_mbs(const void* Aq, const void* As, const void* Am, const void* Bq,
+                   const void* Bs, const void* Bm, int64_t M, int64_t N, int64_t K, void* C,
+                   int out_dtype, hipStream_t stream);
+
+/*
  * Fused linear-layer products ([P1] C.1, C.2, C.3). Each quantizes both
  * operands with the same `hadamard` and `scale_mode`, rotating along the
  * product's reduction axis, into the caller's workspace `ws` (ws_bytes >=
  * mxfp4_workspace_bytes(op, T, N, K), 256-byte aligned), then runs
- * mxfp4_gemm. Three launches on `stream`. Shapes follow Y = X W^T with
+ * mxfp4_gemm. The two operands are quantized as by mxfp4_quantize_pair (one
+ * launch for every Llama-shaped product), then one GEMM launch, on `stream`. Shapes follow Y = X W^T with
  * X [T][K], W [N][K], Y [T][N]:
  *
  * mxfp4_fprop: Y[T][N]  = X[T][K] W[N][K]^T. X, W quantized row-wise along

@@ -28,9 +28,9 @@ ERROR_STATS_FIELDS = ("sum_e_scale2", "sum_e_dz2", "sum_e_grid2", "dot_scale_gri
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp4.so")
 
 EXPORTS = (
-    "mxfp4_quantize", "mxfp4_quantize_dual", "mxfp4_quantize_of", "mxfp4_quantize_mbs",
+    "mxfp4_quantize", "mxfp4_quantize_pair", "mxfp4_quantize_dual", "mxfp4_quantize_of", "mxfp4_quantize_mbs",
     "mxfp4_quantize_rs", "mxfp4_quantize_sr", "mxfp4_error_stats",
-    "mxfp4_error_stats_noalloc", "mxfp4_gemm", "mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad",
+    "mxfp4_error_stats_noalloc", "mxfp4_gemm", "mxfp4_gemm_mbs", "mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad",
     "mxfp4_workspace_bytes", "mxfp4_status_string",
 )
 
@@ -55,6 +55,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     lib.mxfp4_quantize.argtypes = [p, i64, i64, i32, i32, i32, p, p, p]
     lib.mxfp4_quantize.restype = i32
+    lib.mxfp4_quantize_pair.argtypes = [p, i64, i64, i32, p, p, p, i64, i64, i32, p, p, i32, i32, p]
+    lib.mxfp4_quantize_pair.restype = i32
     lib.mxfp4_quantize_dual.argtypes = [p, i64, i64, i32, i32, p, p, p, p, p]
     lib.mxfp4_quantize_dual.restype = i32
     lib.mxfp4_quantize_of.argtypes = [p, i64, i64, i32, i32, i32, p, p, p]
@@ -71,6 +73,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mxfp4_error_stats_noalloc.restype = i32
     lib.mxfp4_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
     lib.mxfp4_gemm.restype = i32
+    lib.mxfp4_gemm_mbs.argtypes = [p, p, p, p, p, p, i64, i64, i64, p, i32, p]
+    lib.mxfp4_gemm_mbs.restype = i32
     for name in ("mxfp4_fprop", "mxfp4_dgrad", "mxfp4_wgrad"):
         fn = getattr(lib, name)
         fn.argtypes = [p, p, i64, i64, i64, i32, i32, p, sz, p, i32, p]
@@ -129,6 +133,23 @@ def mxfp4_quantize(src, rows, cols, axis, hadamard, scale_mode, out_nibbles, out
     _check(load_library().mxfp4_quantize(_ptr(src), rows, cols, axis, hadamard, scale_mode,
                                          _ptr(out_nibbles), _ptr(out_e8m0), _stream(stream)),
            "mxfp4_quantize")
+
+
+def mxfp4_quantize_pair(src_a, rows_a, cols_a, axis_a, nibbles_a, e8m0_a, src_b, rows_b, cols_b,
+                        axis_b, nibbles_b, e8m0_b, hadamard, scale_mode, stream=None):
+    """Both operands of a product (each as mxfp4_quantize) in one launch
+    where the shapes allow it."""
+    import torch
+    for src, rows, cols, axis, nb, sc, w in ((src_a, rows_a, cols_a, axis_a, nibbles_a, e8m0_a, "a"),
+                                             (src_b, rows_b, cols_b, axis_b, nibbles_b, e8m0_b, "b")):
+        _need(src, torch.bfloat16, rows * cols, "src_" + w)
+        n, ns = packed_sizes(rows, cols, axis)
+        _need(nb, torch.uint8, n, "nibbles_" + w)
+        _need(sc, torch.uint8, ns, "e8m0_" + w)
+    _check(load_library().mxfp4_quantize_pair(
+        _ptr(src_a), rows_a, cols_a, axis_a, _ptr(nibbles_a), _ptr(e8m0_a), _ptr(src_b), rows_b,
+        cols_b, axis_b, _ptr(nibbles_b), _ptr(e8m0_b), hadamard, scale_mode, _stream(stream)),
+        "mxfp4_quantize_pair")
 
 
 def mxfp4_quantize_dual(src, rows, cols, hadamard, scale_mode, row_nibbles, row_e8m0,
@@ -236,6 +257,21 @@ def mxfp4_gemm(Aq, As, Bq, Bs, M, N, K, C, out_dtype=OUT_F32, stream=None):
     _need(C, torch.float32 if out_dtype == OUT_F32 else torch.bfloat16, M * N, "C")
     _check(load_library().mxfp4_gemm(_ptr(Aq), _ptr(As), _ptr(Bq), _ptr(Bs), M, N, K, _ptr(C),
                                      out_dtype, _stream(stream)), "mxfp4_gemm")
+
+
+def mxfp4_gemm_mbs(Aq, As, Am, Bq, Bs, Bm, M, N, K, C, out_dtype=OUT_F32, stream=None):
+    """C[M][N] = (deq(A) / cA) (deq(B) / cB)^T from two MBS operands."""
+    import torch
+    _need(Aq, torch.uint8, M * K // 2, "Aq")
+    _need(As, torch.uint8, M * K // 32, "As")
+    _need(Am, torch.uint8, M * K // 128, "Am")
+    _need(Bq, torch.uint8, N * K // 2, "Bq")
+    _need(Bs, torch.uint8, N * K // 32, "Bs")
+    _need(Bm, torch.uint8, N * K // 128, "Bm")
+    _need(C, torch.float32 if out_dtype == OUT_F32 else torch.bfloat16, M * N, "C")
+    _check(load_library().mxfp4_gemm_mbs(_ptr(Aq), _ptr(As), _ptr(Am), _ptr(Bq), _ptr(Bs),
+                                         _ptr(Bm), M, N, K, _ptr(C), out_dtype,
+                                         _stream(stream)), "mxfp4_gemm_mbs")
 
 
 def _fused(name, op, P, Q, T, N, K, hadamard, scale_mode, ws, out, out_dtype, stream, pshape,

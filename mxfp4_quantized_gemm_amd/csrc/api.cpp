@@ -130,11 +130,9 @@ int run_fused(int op, const void* P, const void* Q, int64_t T, int64_t N, int64_
   uint8_t* a_sc = a_nib + round256(p.a.nib_bytes());
   uint8_t* b_nib = a_sc + round256(p.a.sc_bytes());
   uint8_t* b_sc = b_nib + round256(p.b.nib_bytes());
-  hipError_t e = mx::launch_quantize(P, p.a.rows, p.a.cols, p.a.axis, hadamard, scale_mode, a_nib,
-                                     a_sc, stream);
-  if (e != hipSuccess) return MXFP4_ERR_HIP;
-  e = mx::launch_quantize(Q, p.b.rows, p.b.cols, p.b.axis, hadamard, scale_mode, b_nib, b_sc,
-                          stream);
+  const hipError_t e = mx::launch_quantize_pair(P, p.a.rows, p.a.cols, p.a.axis, a_nib, a_sc, Q,
+                                                p.b.rows, p.b.cols, p.b.axis, b_nib, b_sc,
+                                                hadamard, scale_mode, stream);
   if (e != hipSuccess) return MXFP4_ERR_HIP;
   return hip_status(mx::launch_gemm(a_nib, a_sc, b_nib, b_sc, p.M, p.N, p.K, out, out_dtype, stream));
 }
@@ -150,6 +148,28 @@ int mxfp4_quantize(const void* src_bf16, int64_t rows, int64_t cols, int axis, i
   if (st != MXFP4_OK || rows == 0 || cols == 0) return st;
   return hip_status(mx::launch_quantize(src_bf16, rows, cols, axis, hadamard, scale_mode,
                                         out_nibbles, out_e8m0, stream));
+}
+
+int mxfp4_quantize_pair(const void* src_a, int64_t rows_a, int64_t cols_a, int axis_a,
+                        void* nibbles_a, void* e8m0_a, const void* src_b, int64_t rows_b,
+                        int64_t cols_b, int axis_b, void* nibbles_b, void* e8m0_b, int hadamard,
+                        int scale_mode, hipStream_t stream) {
+  if (axis_a == MXFP4_AXIS_2D32 || axis_b == MXFP4_AXIS_2D32) return MXFP4_ERR_MODE;
+  int st = check_quantize(src_a, rows_a, cols_a, axis_a, hadamard, scale_mode, nibbles_a, e8m0_a);
+  if (st == MXFP4_OK)
+    st = check_quantize(src_b, rows_b, cols_b, axis_b, hadamard, scale_mode, nibbles_b, e8m0_b);
+  if (st != MXFP4_OK) return st;
+  const bool ea = rows_a == 0 || cols_a == 0, eb = rows_b == 0 || cols_b == 0;
+  if (ea && eb) return MXFP4_OK;
+  if (ea || eb) {  // one empty operand: the other alone
+    return hip_status(ea ? mx::launch_quantize(src_b, rows_b, cols_b, axis_b, hadamard, scale_mode,
+                                               nibbles_b, e8m0_b, stream)
+                         : mx::launch_quantize(src_a, rows_a, cols_a, axis_a, hadamard, scale_mode,
+                                               nibbles_a, e8m0_a, stream));
+  }
+  return hip_status(mx::launch_quantize_pair(src_a, rows_a, cols_a, axis_a, nibbles_a, e8m0_a,
+                                             src_b, rows_b, cols_b, axis_b, nibbles_b, e8m0_b,
+                                             hadamard, scale_mode, stream));
 }
 
 int mxfp4_quantize_dual(const void* src_bf16, int64_t rows, int64_t cols, int hadamard,
@@ -247,6 +267,17 @@ int mxfp4_gemm(const void* Aq, const void* As, const void* Bq, const void* Bs, i
   const int st = check_gemm(Aq, As, Bq, Bs, M, N, K, C, out_dtype);
   if (st != MXFP4_OK) return st;
   return hip_status(mx::launch_gemm(Aq, As, Bq, Bs, M, N, K, C, out_dtype, stream));
+}
+
+int mxfp4_gemm_mbs(const void* Aq, const void* As, const void* Am, const void* Bq,
+                   const void* Bs, const void* Bm, int64_t M, int64_t N, int64_t K, void* C,
+                   int out_dtype, hipStream_t stream) {
+  const int st = check_gemm(Aq, As, Bq, Bs, M, N, K, C, out_dtype);
+  if (st != MXFP4_OK) return st;
+  if (K % 128) return MXFP4_ERR_SHAPE;
+  if (!Am || !Bm) return MXFP4_ERR_NULL;
+  return hip_status(
+      mx::launch_gemm_mbs(Aq, As, Am, Bq, Bs, Bm, M, N, K, C, out_dtype, stream));
 }
 
 int mxfp4_fprop(const void* X, const void* W, int64_t T, int64_t N, int64_t K, int hadamard,

@@ -230,6 +230,168 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ A
 }
 
 
+// ==================================================== macro-block-scaled GEMM
+// The product of two MBS operands ([P3] "three targeted fixes" section,
+// MBS: x_hat = Q((1 + m) x) / (1 + m) per 128-element macro-block, the
+// postscale undoing the prescale): C[m][n] = sum over macro-blocks g of
+// P_g[m][n] / (cA[m][g] cB[n][g]), with P_g the MXFP4 product of the
+// prescaled operands over the 128 k-values of g and c = 1 + mantissa / 256.
+// The factor varies along k, so it cannot join the power-of-two E8M0
+// scales: each macro-block is two MFMA k-steps accumulated into a temporary
+// set of registers from zero, then added to the result times
+// fl32(fl32(1 / cA) fl32(1 / cB)). Tiles and staging are the general
+// kernel's (128 x 128, 4 waves of 64 x 64); each stage adds the
+// reciprocals 1 / c of its two macro-blocks for the tile's A and B rows, as
+// fp32 in LDS ([2][BM + BN]). K % 128 == 0; rows past M or N and a half
+// k-tile past K take factor 1 (their products are zero).
+constexpr int MBS_R = 2 * (BM + BN) * 4;    // reciprocals of one stage, bytes
+constexpr int STAGE_MBS = STAGE + MBS_R;
+
+__device__ __forceinline__ void load_mbs(float (&r)[2], const uint8_t* __restrict__ Am,
+                                         const uint8_t* __restrict__ Bm, int64_t m0, int64_t n0,
+                                         int64_t M, int64_t N, int64_t kmb, int kt, int t) {
+  const int srow = t & 127;
+  const bool isA = t < 128;
+  const int64_t grow = (isA ? m0 : n0) + srow;
+  const uint8_t* Mm = isA ? Am : Bm;
+  const bool in = grow < (isA ? M : N);
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int64_t mb = (int64_t)kt * 2 + g;
+    const uint32_t m = (in && mb < kmb) ? Mm[grow * kmb + mb] : 0u;
+    r[g] = 1.0f / (1.0f + (float)m * (1.0f / 256.0f));  // c exact in fp32, one rounded division
+  }
+}
+
+__device__ __forceinline__ void store_mbs(const float (&r)[2], uint8_t* stage, int t) {
+  float* lr = reinterpret_cast<float*>(stage + STAGE);
+#pragma unroll
+  for (int g = 0; g < 2; ++g) lr[g * (BM + BN) + t] = r[g];  // t < 128: A row t, else B row t - 128
+}
+
+__device__ __forceinline__ void compute_tile_mbs(const uint8_t* stage, v16f (&acc)[2][2], int wm,
+                                                 int wn, int lane) {
+  const uint8_t* la = stage;
+  const uint8_t* lb = stage + TILE_A;
+  const uint8_t* ls = stage + TILE_A + TILE_B;
+  const float* lr = reinterpret_cast<const float*>(stage + STAGE);
+  const int half = lane >> 5;
+  uint32_t sa[2][2], sb[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ar = wm * 64 + i * 32 + (lane & 31);
+    const int br = wn * 64 + i * 32 + (lane & 31);
+    const uint64_t va = *reinterpret_cast<const uint64_t*>(ls + ar * BKS) >> (8 * half);
+    const uint64_t vb = *reinterpret_cast<const uint64_t*>(ls + (BM + br) * BKS) >> (8 * half);
+    sa[i][0] = (uint32_t)va;
+    sa[i][1] = (uint32_t)(va >> 32);
+    sb[i][0] = (uint32_t)vb;
+    sb[i][1] = (uint32_t)(vb >> 32);
+  }
+  const v16f zero = {};
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {  // macro-block g: k-steps 2 g and 2 g + 1
+    v16f tmp[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int s = 2 * g + u;
+      v8i af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = frag(la, wm * 64 + i * 32 + (lane & 31), 2 * s + half);
+        bf[i] = frag(lb, wn * 64 + i * 32 + (lane & 31), 2 * s + half);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int wa = (int)sa[i][s >> 1], wb = (int)sb[j][s >> 1];
+          const v16f c = u == 0 ? zero : tmp[i][j];
+          tmp[i][j] = (s & 1) ? mfma<2>(af[i], bf[j], c, wa, wb) : mfma<0>(af[i], bf[j], c, wa, wb);
+        }
+    }
+    // lane: column (lane & 31) of each 32 x 32 tile, rows 8 q + 4 half + e
+    float rb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) rb[j] = lr[g * (BM + BN) + BM + wn * 64 + j * 32 + (lane & 31)];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 ra =
+            *reinterpret_cast<const float4*>(lr + g * (BM + BN) + wm * 64 + i * 32 + 8 * q + 4 * half);
+        const float rv[4] = {ra.x, ra.y, ra.z, ra.w};
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[i][j][4 * q + e] = fmaf(tmp[i][j][4 * q + e], rv[e] * rb[j], acc[i][j][4 * q + e]);
+      }
+  }
+}
+
+template <int OUT, bool SCALE_VEC>
+__global__ __launch_bounds__(256) void gemm_mbs_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ Am,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, const uint8_t* __restrict__ Bm,
+    int64_t M, int64_t N, int64_t K, void* __restrict__ C) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE_MBS];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t ntn = (N + BN - 1) / BN;
+  const int64_t tm = (int64_t)blockIdx.x / ntn, tn = (int64_t)blockIdx.x % ntn;
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const int64_t kbytes = K / 2, kblk = K / 32, kmb = K / 128;
+  const int nkt = (int)((kbytes + BKB - 1) / BKB);
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  TileRegs R;
+  float rm[2];
+  load_tile<SCALE_VEC>(R, A, As, B, Bs, m0, n0, M, N, kbytes, kblk, 0, t);
+  load_mbs(rm, Am, Bm, m0, n0, M, N, kmb, 0, t);
+  store_tile(R, lds, t);
+  store_mbs(rm, lds, t);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const bool more = kt + 1 < nkt;
+    if (more) {
+      load_tile<SCALE_VEC>(R, A, As, B, Bs, m0, n0, M, N, kbytes, kblk, kt + 1, t);
+      load_mbs(rm, Am, Bm, m0, n0, M, N, kmb, kt + 1, t);
+    }
+    compute_tile_mbs(lds + (kt & 1) * STAGE_MBS, acc, wm, wn, lane);
+    if (more) {
+      store_tile(R, lds + ((kt + 1) & 1) * STAGE_MBS, t);
+      store_mbs(rm, lds + ((kt + 1) & 1) * STAGE_MBS, t);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < M) {
+          if (OUT == 0)
+            static_cast<float*>(C)[row * N + col] = acc[i][j][r];
+          else
+            static_cast<uint16_t*>(C)[row * N + col] = (uint16_t)bf16_rne(acc[i][j][r]);
+        }
+      }
+    }
+}
+
 // ====================================================== large-tile kernel
 // For K % 256 == 0 (every Llama shape). Templated on the wave layout: WM x WN
 // waves per work-group, each computing TM x TN MFMA 32x32x64 tiles, so the
@@ -1263,6 +1425,36 @@ hipError_t launch(const uint8_t* a, const uint8_t* as, const uint8_t* b, const u
 }  // namespace dm
 
 }  // namespace
+
+hipError_t launch_gemm_mbs(const void* Aq, const void* As, const void* Am, const void* Bq,
+                           const void* Bs, const void* Bm, int64_t M, int64_t N, int64_t K,
+                           void* C, int out_dtype, hipStream_t stream) {
+  const auto* a = static_cast<const uint8_t*>(Aq);
+  const auto* as = static_cast<const uint8_t*>(As);
+  const auto* am = static_cast<const uint8_t*>(Am);
+  const auto* b = static_cast<const uint8_t*>(Bq);
+  const auto* bs = static_cast<const uint8_t*>(Bs);
+  const auto* bm = static_cast<const uint8_t*>(Bm);
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const bool svec = (K % 256 == 0) && ((uintptr_t)As % 8 == 0) && ((uintptr_t)Bs % 8 == 0);
+  const dim3 grid((unsigned)tiles), blk(256);
+  if (out_dtype == 0) {
+    if (svec)
+      hipLaunchKernelGGL((gemm_mbs_kernel<0, true>), grid, blk, 0, stream, a, as, am, b, bs, bm, M,
+                         N, K, C);
+    else
+      hipLaunchKernelGGL((gemm_mbs_kernel<0, false>), grid, blk, 0, stream, a, as, am, b, bs, bm,
+                         M, N, K, C);
+  } else {
+    if (svec)
+      hipLaunchKernelGGL((gemm_mbs_kernel<1, true>), grid, blk, 0, stream, a, as, am, b, bs, bm, M,
+                         N, K, C);
+    else
+      hipLaunchKernelGGL((gemm_mbs_kernel<1, false>), grid, blk, 0, stream, a, as, am, b, bs, bm,
+                         M, N, K, C);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(const void* Aq, const void* As, const void* Bq, const void* Bs, int64_t M,
                        int64_t N, int64_t K, void* C, int out_dtype, hipStream_t stream) {

@@ -11,6 +11,13 @@ hipError_t launch_quantize(const void* src, int64_t rows, int64_t cols, int axis
                            int hadamard, int scale_mode, void* nib, void* sc,
                            hipStream_t stream);
 
+// Two operands (as two launch_quantize calls with the same rotation and
+// scale rule) in one launch where both shapes allow it, else two launches.
+hipError_t launch_quantize_pair(const void* src_a, int64_t rows_a, int64_t cols_a, int axis_a,
+                                void* nib_a, void* sc_a, const void* src_b, int64_t rows_b,
+                                int64_t cols_b, int axis_b, void* nib_b, void* sc_b,
+                                int hadamard, int scale_mode, hipStream_t stream);
+
 // One read of src, two outputs: row-wise (rnib, rsc) and column-wise
 // transposed (cnib, csc), each as launch_quantize with axis ROW / COL.
 hipError_t launch_quantize_dual(const void* src, int64_t rows, int64_t cols, int hadamard,
@@ -55,5 +62,12 @@ hipError_t launch_error_stats_noalloc(const void* src, int64_t rows, int64_t col
 hipError_t launch_gemm(const void* Aq, const void* As, const void* Bq, const void* Bs,
                        int64_t M, int64_t N, int64_t K, void* C, int out_dtype,
                        hipStream_t stream);
+
+// GEMM of two macro-block-scaled operands (mantissa bytes Am [M][K/128],
+// Bm [N][K/128]): C = sum over 128-k macro-blocks of the MXFP4 product times
+// 1 / ((1 + mA / 256) (1 + mB / 256)). K % 128 == 0.
+hipError_t launch_gemm_mbs(const void* Aq, const void* As, const void* Am, const void* Bq,
+                           const void* Bs, const void* Bm, int64_t M, int64_t N, int64_t K,
+                           void* C, int out_dtype, hipStream_t stream);
 
 }  // namespace mx

@@ -47,11 +47,9 @@ __device__ __forceinline__ uint4 ld_nt16(const uint16_t* p) {
 // multiple of 32 long, so block b covers elements [32b, 32b + 32) of the
 // flat array and owns nibble bytes [16b, 16b + 16) and scale byte b.
 template <int H, int MODE>
-__global__ __launch_bounds__(256) void quant_row_kernel(const uint4* __restrict__ src,
-                                                        int64_t nblocks,
-                                                        uint4* __restrict__ nib,
-                                                        uint8_t* __restrict__ sc) {
-  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void row_block(const uint4* __restrict__ src, int64_t nblocks,
+                                          uint4* __restrict__ nib, uint8_t* __restrict__ sc,
+                                          int64_t b) {
   if (b >= nblocks) return;
   uint4 q[4];
 #pragma unroll
@@ -64,6 +62,14 @@ __global__ __launch_bounds__(256) void quant_row_kernel(const uint4* __restrict_
   encode_block_sh<MODE, kScaleShift<H>>(v, out, s);
   nib[b] = out;
   sc[b] = (uint8_t)s;
+}
+
+template <int H, int MODE>
+__global__ __launch_bounds__(256) void quant_row_kernel(const uint4* __restrict__ src,
+                                                        int64_t nblocks,
+                                                        uint4* __restrict__ nib,
+                                                        uint8_t* __restrict__ sc) {
+  row_block<H, MODE>(src, nblocks, nib, sc, (int64_t)blockIdx.x * 256 + threadIdx.x);
 }
 
 // Lane-contiguous variant (nblocks % 64 == 0): a wave owns 64 consecutive
@@ -92,12 +98,10 @@ __device__ __forceinline__ void quad_transpose(uint32_t (&x)[4], int p) {
   if (b0) { x[0] = u0; x[2] = u1; } else { x[1] = u0; x[3] = u1; }
 }
 
+// Blocks b0 .. b0 + 63 by one wave.
 template <int H, int MODE>
-__global__ __launch_bounds__(256) void quant_row_lc_kernel(const uint4* __restrict__ src,
-                                                           uint4* __restrict__ nib,
-                                                           uint8_t* __restrict__ sc) {
-  const int lane = threadIdx.x & 63;
-  const int64_t b0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;
+__device__ __forceinline__ void row_lc_wave(const uint4* __restrict__ src, uint4* __restrict__ nib,
+                                            uint8_t* __restrict__ sc, int64_t b0, int lane) {
   const nt_u32x4* s4 = reinterpret_cast<const nt_u32x4*>(src);
   uint4 q[4];
 #pragma unroll
@@ -128,6 +132,14 @@ __global__ __launch_bounds__(256) void quant_row_lc_kernel(const uint4* __restri
   encode_block_sh<MODE, kScaleShift<H>>(v, out, s);
   nib[b] = out;
   sc[b] = (uint8_t)s;
+}
+
+template <int H, int MODE>
+__global__ __launch_bounds__(256) void quant_row_lc_kernel(const uint4* __restrict__ src,
+                                                           uint4* __restrict__ nib,
+                                                           uint8_t* __restrict__ sc) {
+  row_lc_wave<H, MODE>(src, nib, sc, ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64,
+                       threadIdx.x & 63);
 }
 
 // ----------------------------------------------------------- 2D (32x32 tile)
@@ -237,18 +249,17 @@ __global__ __launch_bounds__(256) void quant_col_kernel(const uint16_t* __restri
 // scattered 16-byte and 1-byte stores. Four columns per lane keep the
 // register count low enough for several waves per SIMD, so the loads of one
 // wave overlap the arithmetic of another.
-template <int H, int MODE, int NB, bool RS = false>
-__global__ __launch_bounds__(64 * NB) void quant_col_staged_kernel(const uint16_t* __restrict__ src,
-                                                                   int64_t rows, int64_t cols,
-                                                                   uint8_t* __restrict__ nib,
-                                                                   uint8_t* __restrict__ sc,
-                                                                   const uint8_t* __restrict__ signs) {
+template <int H, int MODE, int NB, bool RS>
+__device__ __forceinline__ void col_staged_wg(const uint16_t* __restrict__ src, int64_t rows,
+                                              int64_t cols, uint8_t* __restrict__ nib,
+                                              uint8_t* __restrict__ sc,
+                                              const uint8_t* __restrict__ signs, int64_t wg) {
   __shared__ __attribute__((aligned(16))) uint8_t onib[256 * NB * 16];
   __shared__ __attribute__((aligned(16))) uint8_t osc[256 * NB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t ncg = (cols + 255) / 256;
-  const int64_t cg = (int64_t)blockIdx.x % ncg;
-  const int64_t rg = (int64_t)blockIdx.x / ncg;
+  const int64_t cg = wg % ncg;
+  const int64_t rg = wg / ncg;
   const int64_t band = rg * NB + wave;
   const int64_t c0 = cg * 256 + (int64_t)lane * 4;
   if (c0 < cols) {
@@ -302,6 +313,15 @@ __global__ __launch_bounds__(64 * NB) void quant_col_staged_kernel(const uint16_
             *reinterpret_cast<const uint32_t*>(osc + threadIdx.x * 4);
     }
   }
+}
+
+template <int H, int MODE, int NB, bool RS = false>
+__global__ __launch_bounds__(64 * NB) void quant_col_staged_kernel(const uint16_t* __restrict__ src,
+                                                                   int64_t rows, int64_t cols,
+                                                                   uint8_t* __restrict__ nib,
+                                                                   uint8_t* __restrict__ sc,
+                                                                   const uint8_t* __restrict__ signs) {
+  col_staged_wg<H, MODE, NB, RS>(src, rows, cols, nib, sc, signs, blockIdx.x);
 }
 
 // Scalar path for any cols: one thread per (column, 32-row band); loads are
@@ -930,10 +950,13 @@ hipError_t dispatch_axis(const void* src, int64_t rows, int64_t cols, int axis, 
   if (axis == 0) {
     const int64_t nblocks = rows * (cols / 32);
     const int64_t grid = (nblocks + 255) / 256;
-    // The lane-contiguous kernel wins on large tensors; on 8192 x 4096 and
-    // below, and inside the Llama step (after a GEMM), the one-block-per-
-    // thread kernel was as fast or faster (in-step A/B: 17.5 vs 20.5 us).
-    if (nblocks % 256 == 0 && nblocks > (int64_t(1) << 20))
+    // Launched on its own, the lane-contiguous kernel is as fast or faster at
+    // every size measured (back to back over six buffer sets: 8192 x 4096
+    // 15.3 against 16.8 us, 6144 x 4096 12.1 against 12.9 us, 28672 x 4096
+    // equal). Inside the Llama step, right after a GEMM, the one-block-per-
+    // thread body is faster below 2^20 blocks; the two-operand launch
+    // (launch_quantize_pair) keeps that choice.
+    if (nblocks % 256 == 0)
       hipLaunchKernelGGL((quant_row_lc_kernel<H, MODE>), dim3((unsigned)grid), blk, 0, st,
                          static_cast<const uint4*>(src), static_cast<uint4*>(nib),
                          static_cast<uint8_t*>(sc));
@@ -1197,7 +1220,120 @@ hipError_t dispatch_sr(const void* src, int64_t rows, int64_t cols, int axis, co
   return hipGetLastError();
 }
 
+// ------------------------------------------------ two operands in one launch
+// A product quantizes two operands; one launch over both grids saves a
+// launch's ramp and tail. Work-groups [0, ga) run operand A's kernel body,
+// the rest operand B's. Both bodies run with 512-thread work-groups: the
+// row kernels take 512 blocks per work-group (one per thread, or 64 per
+// wave in the lane-contiguous form), the column kernel its 8-band staged
+// form. Each body and its results are exactly those of its own launch.
+struct QJob {
+  const void* src;
+  int64_t rows, cols;
+  void* nib;
+  void* sc;
+};
+
+template <int H, int MODE>
+struct RowBody {
+  static int64_t groups(const QJob& j) { return (j.rows * (j.cols / 32) + 511) / 512; }
+  __device__ static void run(const QJob& j, int64_t wg) {
+    row_block<H, MODE>(static_cast<const uint4*>(j.src), j.rows * (j.cols / 32),
+                       static_cast<uint4*>(j.nib), static_cast<uint8_t*>(j.sc),
+                       wg * 512 + threadIdx.x);
+  }
+};
+
+template <int H, int MODE>
+struct RowLcBody {  // blocks % 512 == 0
+  static int64_t groups(const QJob& j) { return j.rows * (j.cols / 32) / 512; }
+  __device__ static void run(const QJob& j, int64_t wg) {
+    row_lc_wave<H, MODE>(static_cast<const uint4*>(j.src), static_cast<uint4*>(j.nib),
+                         static_cast<uint8_t*>(j.sc), (wg * 8 + (threadIdx.x >> 6)) * 64,
+                         threadIdx.x & 63);
+  }
+};
+
+template <int H, int MODE>
+struct ColBody {  // rows % 256 == 0, cols % 4 == 0, scales 8-byte aligned
+  static int64_t groups(const QJob& j) { return (j.rows / 256) * ((j.cols + 255) / 256); }
+  __device__ static void run(const QJob& j, int64_t wg) {
+    col_staged_wg<H, MODE, 8, false>(static_cast<const uint16_t*>(j.src), j.rows, j.cols,
+                                     static_cast<uint8_t*>(j.nib), static_cast<uint8_t*>(j.sc),
+                                     nullptr, wg);
+  }
+};
+
+template <class BA, class BB>
+__global__ __launch_bounds__(512) void quant_pair_kernel(QJob a, QJob b, int64_t ga) {
+  const int64_t wg = blockIdx.x;
+  if (wg < ga)
+    BA::run(a, wg);
+  else
+    BB::run(b, wg - ga);
+}
+
+// Which body serves an operand in a pair launch: 0 row, 1 row lane-
+// contiguous, 2 column; -1 when its shape needs a kernel of its own. Rows:
+// lane-contiguous above 2^20 blocks only; in the Llama step (after a GEMM)
+// it made the qkv pair of 8192 x 4096 and 6144 x 4096 slower (34.8 against
+// 29.2 us), unlike a launch on its own (dispatch_axis).
+int pair_kind(int64_t rows, int64_t cols, int axis, const void* sc) {
+  if (axis == 0) {
+    const int64_t nblocks = rows * (cols / 32);
+    return (nblocks % 512 == 0 && nblocks > (int64_t(1) << 20)) ? 1 : 0;
+  }
+  if (axis == 1 && rows % 256 == 0 && cols % 4 == 0 && ((uintptr_t)sc % 8 == 0)) return 2;
+  return -1;
+}
+
+template <int H, int MODE, class BA>
+hipError_t pair_b(const QJob& a, const QJob& b, int kb, hipStream_t st) {
+  const int64_t ga = BA::groups(a);
+  const auto go = [&](auto bb) {
+    using BB = decltype(bb);
+    hipLaunchKernelGGL((quant_pair_kernel<BA, BB>), dim3((unsigned)(ga + BB::groups(b))),
+                       dim3(512), 0, st, a, b, ga);
+    return hipGetLastError();
+  };
+  if (kb == 0) return go(RowBody<H, MODE>{});
+  if (kb == 1) return go(RowLcBody<H, MODE>{});
+  return go(ColBody<H, MODE>{});
+}
+
+template <int H, int MODE>
+hipError_t dispatch_pair(const QJob& a, int axa, const QJob& b, int axb, hipStream_t st) {
+  const int ka = pair_kind(a.rows, a.cols, axa, a.sc), kb = pair_kind(b.rows, b.cols, axb, b.sc);
+  if (ka < 0 || kb < 0) {
+    hipError_t e = dispatch_axis<H, MODE>(a.src, a.rows, a.cols, axa, a.nib, a.sc, st);
+    if (e != hipSuccess) return e;
+    return dispatch_axis<H, MODE>(b.src, b.rows, b.cols, axb, b.nib, b.sc, st);
+  }
+  if (ka == 0) return pair_b<H, MODE, RowBody<H, MODE>>(a, b, kb, st);
+  if (ka == 1) return pair_b<H, MODE, RowLcBody<H, MODE>>(a, b, kb, st);
+  return pair_b<H, MODE, ColBody<H, MODE>>(a, b, kb, st);
+}
+
+template <int H>
+hipError_t dispatch_pair_mode(const QJob& a, int axa, const QJob& b, int axb, int mode,
+                              hipStream_t st) {
+  return mode == kCeil ? dispatch_pair<H, kCeil>(a, axa, b, axb, st)
+                       : dispatch_pair<H, kOcpFloor>(a, axa, b, axb, st);
+}
+
 }  // namespace
+
+hipError_t launch_quantize_pair(const void* src_a, int64_t rows_a, int64_t cols_a, int axis_a,
+                                void* nib_a, void* sc_a, const void* src_b, int64_t rows_b,
+                                int64_t cols_b, int axis_b, void* nib_b, void* sc_b,
+                                int hadamard, int scale_mode, hipStream_t stream) {
+  const QJob a{src_a, rows_a, cols_a, nib_a, sc_a}, b{src_b, rows_b, cols_b, nib_b, sc_b};
+  switch (hadamard) {
+    case 16: return dispatch_pair_mode<16>(a, axis_a, b, axis_b, scale_mode, stream);
+    case 32: return dispatch_pair_mode<32>(a, axis_a, b, axis_b, scale_mode, stream);
+    default: return dispatch_pair_mode<0>(a, axis_a, b, axis_b, scale_mode, stream);
+  }
+}
 
 hipError_t launch_quantize(const void* src, int64_t rows, int64_t cols, int axis, int hadamard,
                            int scale_mode, void* nib, void* sc, hipStream_t stream) {

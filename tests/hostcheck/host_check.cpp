@@ -108,6 +108,38 @@ void quantize_cases() {
   CHECK(mxfp4_error_stats_noalloc(src, 32, 64, 1, 32, 1, out, nullptr) == MXFP4_OK);
   CHECK(stub::g_ncalls == 2 && strcmp(stub::g_calls[1].what, "stats_noalloc") == 0);
   CHECK(stub::g_calls[1].out[0] == out && stub::g_calls[1].i[1] == 32);
+
+  // two operands in one call: each validated as mxfp4_quantize, A first
+  void* src2 = at(36864);
+  void* nib2 = at(40960);
+  void* sc2 = at(45056);
+  stub::reset(hipSuccess);
+  CHECK(mxfp4_quantize_pair(src, 64, 64, 2, nib, sc, src2, 64, 64, 0, nib2, sc2, 16, 0,
+                            nullptr) == MXFP4_ERR_MODE);
+  CHECK(mxfp4_quantize_pair(src, 64, 48, 0, nib, sc, src2, 64, 64, 0, nib2, sc2, 16, 0,
+                            nullptr) == MXFP4_ERR_SHAPE);
+  CHECK(mxfp4_quantize_pair(src, 64, 64, 0, nib, sc, src2, 48, 64, 1, nib2, sc2, 16, 0,
+                            nullptr) == MXFP4_ERR_SHAPE);
+  CHECK(mxfp4_quantize_pair(src, 64, 64, 0, nib, sc, nullptr, 64, 64, 1, nib2, sc2, 16, 0,
+                            nullptr) == MXFP4_ERR_NULL);
+  CHECK(mxfp4_quantize_pair(src, 64, 64, 0, nib, sc, src2, 64, 64, 1, at(40961), sc2, 16, 0,
+                            nullptr) == MXFP4_ERR_ALIGN);
+  CHECK(mxfp4_quantize_pair(src, 64, 64, 0, nib, sc, src2, 64, 64, 1, nib2, sc2, 12, 0,
+                            nullptr) == MXFP4_ERR_MODE);
+  CHECK(stub::g_ncalls == 0);
+  CHECK(mxfp4_quantize_pair(nullptr, 0, 64, 0, nullptr, nullptr, nullptr, 64, 0, 1, nullptr,
+                            nullptr, 16, 0, nullptr) == MXFP4_OK);
+  CHECK(stub::g_ncalls == 0);
+  CHECK(mxfp4_quantize_pair(nullptr, 0, 64, 0, nullptr, nullptr, src2, 64, 96, 1, nib2, sc2, 32,
+                            1, nullptr) == MXFP4_OK);
+  CHECK(stub::g_ncalls == 1 && strcmp(stub::g_calls[0].what, "quantize") == 0 &&
+        stub::g_calls[0].src == src2 && stub::g_calls[0].i[0] == 1);
+  CHECK(mxfp4_quantize_pair(src, 64, 96, 0, nib, sc, src2, 128, 64, 1, nib2, sc2, 16, 1,
+                            nullptr) == MXFP4_OK);
+  CHECK(stub::g_ncalls == 2 && strcmp(stub::g_calls[1].what, "pair") == 0);
+  CHECK(stub::g_calls[1].d[0] == 64 && stub::g_calls[1].d[1] == 96 && stub::g_calls[1].d[2] == 128);
+  CHECK(stub::g_pair_b[1].src == src2 && stub::g_pair_b[1].cols == 64 && stub::g_pair_b[1].axis == 1);
+  CHECK(stub::g_calls[1].out[2] == nib2 && stub::g_calls[1].out[3] == sc2);
 }
 
 void gemm_cases() {
@@ -135,6 +167,20 @@ void gemm_cases() {
   CHECK(g.out[0] == as && g.out[1] == b && g.out[2] == bs && g.out[3] == at(16386));
   stub::reset(hipErrorLaunchFailure);
   CHECK(mxfp4_gemm(a, as, b, bs, 32, 32, 64, c, 0, nullptr) == MXFP4_ERR_HIP);
+  // the macro-block-scaled product: K % 128, both mantissa arrays
+  void* am = at(20480);
+  void* bm = at(20481);
+  stub::reset(hipSuccess);
+  CHECK(mxfp4_gemm_mbs(a, as, am, b, bs, bm, 32, 32, 96, c, 0, nullptr) == MXFP4_ERR_SHAPE);
+  CHECK(mxfp4_gemm_mbs(a, as, nullptr, b, bs, bm, 32, 32, 128, c, 0, nullptr) == MXFP4_ERR_NULL);
+  CHECK(mxfp4_gemm_mbs(a, as, am, b, bs, nullptr, 32, 32, 128, c, 0, nullptr) == MXFP4_ERR_NULL);
+  CHECK(mxfp4_gemm_mbs(a, as, am, b, bs, bm, 32, 32, 128, at(16386), 0, nullptr) == MXFP4_ERR_ALIGN);
+  CHECK(mxfp4_gemm_mbs(a, as, am, b, bs, bm, 0, 32, 128, c, 0, nullptr) == MXFP4_ERR_SHAPE);
+  CHECK(stub::g_ncalls == 0);
+  CHECK(mxfp4_gemm_mbs(a, as, am, b, bs, bm, 33, 70, 384, c, 1, nullptr) == MXFP4_OK);
+  CHECK(stub::g_ncalls == 1 && strcmp(stub::g_calls[0].what, "gemm_mbs") == 0);
+  CHECK(stub::g_calls[0].d[0] == 33 && stub::g_calls[0].d[1] == 70 && stub::g_calls[0].d[2] == 384);
+  CHECK(stub::g_calls[0].i[0] == 1 && stub::g_calls[0].i[1] == 1);
 }
 
 // One fused product: the two quantize launches and the GEMM, with the
@@ -155,10 +201,10 @@ void fused_case(int op, int64_t T, int64_t N, int64_t K) {
   CHECK(fn(P, Q, T, N, K, 12, 0, ws, need, Y, 0, nullptr) == MXFP4_ERR_MODE);
   CHECK(stub::g_ncalls == 0);
   CHECK(fn(P, Q, T, N, K, 16, 1, ws, need, Y, 1, nullptr) == MXFP4_OK);
-  CHECK(stub::g_ncalls == 3);
-  const stub::Call& qa = stub::g_calls[0];
-  const stub::Call& qb = stub::g_calls[1];
-  const stub::Call& g = stub::g_calls[2];
+  CHECK(stub::g_ncalls == 2 && strcmp(stub::g_calls[0].what, "pair") == 0);
+  const stub::Call& q = stub::g_calls[0];
+  const stub::PairB& pb = stub::g_pair_b[0];
+  const stub::Call& g = stub::g_calls[1];
   // source shapes and axes of the two operands, GEMM sizes
   int64_t ar, ac, br, bc, M, NN, KK;
   int aax, bax;
@@ -169,19 +215,19 @@ void fused_case(int op, int64_t T, int64_t N, int64_t K) {
   } else {
     ar = T; ac = N; aax = 1; br = T; bc = K; bax = 1; M = N; NN = K; KK = T;
   }
-  CHECK(qa.src == P && qa.d[0] == ar && qa.d[1] == ac && qa.i[0] == aax);
-  CHECK(qb.src == Q && qb.d[0] == br && qb.d[1] == bc && qb.i[0] == bax);
-  CHECK(qa.i[1] == 16 && qa.i[2] == 1 && qb.i[1] == 16 && qb.i[2] == 1);
+  CHECK(q.src == P && q.d[0] == ar && q.d[1] == ac && q.i[0] == aax);
+  CHECK(pb.src == Q && q.d[2] == br && pb.cols == bc && pb.axis == bax);
+  CHECK(q.i[1] == 16 && q.i[2] == 1);
   CHECK(g.d[0] == M && g.d[1] == NN && g.d[2] == KK && g.i[0] == 1 && g.out[3] == Y);
   const size_t anib = size_t(M) * size_t(KK / 2), asc = size_t(M) * size_t(KK / 32);
   const size_t bnib = size_t(NN) * size_t(KK / 2), bsc = size_t(NN) * size_t(KK / 32);
   unsigned char* w = ws;
-  CHECK(qa.out[0] == w && qa.out[1] == w + r256(anib));
-  CHECK(qb.out[0] == w + r256(anib) + r256(asc));
-  CHECK(qb.out[1] == w + r256(anib) + r256(asc) + r256(bnib));
+  CHECK(q.out[0] == w && q.out[1] == w + r256(anib));
+  CHECK(q.out[2] == w + r256(anib) + r256(asc));
+  CHECK(q.out[3] == w + r256(anib) + r256(asc) + r256(bnib));
   CHECK(need == r256(anib) + r256(asc) + r256(bnib) + r256(bsc));
-  CHECK(g.src == qa.out[0] && g.out[0] == qa.out[1] && g.out[1] == qb.out[0] &&
-        g.out[2] == qb.out[1]);
+  CHECK(g.src == q.out[0] && g.out[0] == q.out[1] && g.out[1] == q.out[2] &&
+        g.out[2] == q.out[3]);
   // a failed first launch stops the product
   stub::reset(hipErrorInvalidValue);
   CHECK(fn(P, Q, T, N, K, 16, 0, ws, need, Y, 0, nullptr) == MXFP4_ERR_HIP);

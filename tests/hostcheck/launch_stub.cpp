@@ -6,6 +6,7 @@
 
 namespace stub {
 Call g_calls[kMaxCalls];
+PairB g_pair_b[kMaxCalls];
 int g_ncalls = 0;
 hipError_t g_result = hipSuccess;
 
@@ -30,6 +31,19 @@ hipError_t launch_quantize(const void* src, int64_t rows, int64_t cols, int axis
                            int scale_mode, void* nib, void* sc, hipStream_t) {
   return stub::record("quantize", src, rows, cols, axis, hadamard, scale_mode, nib, sc, nullptr,
                       nullptr);
+}
+
+hipError_t launch_quantize_pair(const void* src_a, int64_t rows_a, int64_t cols_a, int axis_a,
+                                void* nib_a, void* sc_a, const void* src_b, int64_t rows_b,
+                                int64_t cols_b, int axis_b, void* nib_b, void* sc_b,
+                                int hadamard, int scale_mode, hipStream_t) {
+  const hipError_t r = stub::record("pair", src_a, rows_a, cols_a, axis_a, hadamard, scale_mode,
+                                    nib_a, sc_a, nib_b, sc_b);
+  if (stub::g_ncalls <= stub::kMaxCalls) {
+    stub::g_calls[stub::g_ncalls - 1].d[2] = rows_b;
+    stub::g_pair_b[stub::g_ncalls - 1] = {src_b, cols_b, axis_b};
+  }
+  return r;
 }
 
 hipError_t launch_quantize_dual(const void* src, int64_t rows, int64_t cols, int hadamard,
@@ -80,6 +94,18 @@ hipError_t launch_gemm(const void* Aq, const void* As, const void* Bq, const voi
   const hipError_t r = stub::record("gemm", Aq, M, N, out_dtype, 0, 0, const_cast<void*>(As),
                                     const_cast<void*>(Bq), const_cast<void*>(Bs), C);
   if (stub::g_ncalls <= stub::kMaxCalls) stub::g_calls[stub::g_ncalls - 1].d[2] = K;
+  return r;
+}
+
+hipError_t launch_gemm_mbs(const void* Aq, const void* As, const void* Am, const void* Bq,
+                           const void* Bs, const void* Bm, int64_t M, int64_t N, int64_t K,
+                           void* C, int out_dtype, hipStream_t) {
+  const hipError_t r = stub::record("gemm_mbs", Aq, M, N, out_dtype, 0, 0, const_cast<void*>(As),
+                                    const_cast<void*>(Bq), const_cast<void*>(Bs), C);
+  if (stub::g_ncalls <= stub::kMaxCalls) {
+    stub::g_calls[stub::g_ncalls - 1].d[2] = K;
+    stub::g_calls[stub::g_ncalls - 1].i[1] = Am != nullptr && Bm != nullptr;
+  }
   return r;
 }
 

@@ -16,6 +16,13 @@ struct Call {
 };
 constexpr int kMaxCalls = 16;
 extern Call g_calls[kMaxCalls];
+// operand B of a pair launch (rows in Call::d[2], outputs in Call::out[2..3])
+struct PairB {
+  const void* src;
+  int64_t cols;
+  int axis;
+};
+extern PairB g_pair_b[kMaxCalls];
 extern int g_ncalls;
 extern hipError_t g_result;  // what every launch returns
 void reset(hipError_t result);

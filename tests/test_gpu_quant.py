@@ -44,7 +44,7 @@ def heavy(rows, cols, seed):
 
 
 SHAPES = {
-    0: [(1, 32), (3, 96), (257, 160), (64, 4128)],
+    0: [(1, 32), (3, 96), (257, 160), (64, 4128), (256, 256), (96, 8192)],
     1: [(32, 1), (64, 7), (32, 100), (96, 520), (128, 1544), (160, 8), (256, 300), (384, 4),
         (128, 260)],
     2: [(32, 32), (64, 96), (96, 320), (32, 4096)],
@@ -137,9 +137,10 @@ def test_quantizer_workload_full_size_other_rotations(quant_workload, h):
 
 @pytest.mark.parametrize("mode", [0, 1])
 def test_row_quantizer_above_lane_contiguous_threshold(quant_workload, mode):
-    """Row-wise quantization of more than 2^20 blocks runs the lane-contiguous
-    kernel (quad-transposed loads): 8448 x 4096 (the workload plus its first
-    256 rows again), every byte."""
+    """More than 2^20 row blocks (8448 x 4096: the workload plus its first
+    256 rows again), every byte: the lane-contiguous kernel (quad-transposed
+    loads), which the standalone quantizer runs whenever the block count is
+    a multiple of 256 and the two-operand launch above 2^20 blocks."""
     big = np.concatenate([quant_workload, quant_workload[:256]], axis=0)
     assert_same(big, AXES["row"], 16, mode, f"row 8448x4096 mode={mode}")
 
@@ -227,3 +228,37 @@ def test_e2m1_encode_exhaustive(mode):
     bits = exhaustive_encode_matrix(mode)
     assert_same(bits, 0, 0, mode, f"exhaustive encode row mode={mode}")
     assert_same(np.ascontiguousarray(bits.T), 1, 0, mode, f"exhaustive encode col mode={mode}")
+
+
+PAIRS = [
+    (((300, 640), 0), ((128, 96), 0)),        # row + row
+    (((4096, 8320), 0), ((96, 320), 0)),      # lane-contiguous row (> 2^20 blocks) + row
+    (((64, 256), 0), ((512, 260), 1)),        # row + column (8-band staged)
+    (((256, 100), 1), ((768, 36), 1)),        # column + column
+    (((512, 64), 1), ((4096, 8320), 0)),      # column + lane-contiguous row
+    (((96, 64), 1), ((64, 96), 0)),           # column shape without the staged form: two launches
+]
+
+
+@pytest.mark.parametrize("pair", PAIRS)
+@pytest.mark.parametrize("h,mode", [(16, 0), (32, 1), (0, 1)])
+def test_pair_launch_bit_exact(pair, h, mode):
+    """mxfp4_quantize_pair: both operands byte for byte the oracle's."""
+    import torch
+    import mxfp4_quantized_gemm_amd as mx
+    bits, outs = [], []
+    for k, ((r, c), axis) in enumerate(pair):
+        b = heavy(r, c, 4400 + 3 * k + r % 7)
+        ns, ss = mx.packed_shapes(r, c, axis)
+        bits.append((b, axis))
+        outs.append((to_dev_bf16(b), torch.full(ns, 0xAB, dtype=torch.uint8, device="cuda"),
+                     torch.full(ss, 0xAB, dtype=torch.uint8, device="cuda")))
+    (ba, axa), (bb, axb) = bits
+    (xa, na, sa), (xb, nb, sb) = outs
+    mx.mxfp4_quantize_pair(xa, ba.shape[0], ba.shape[1], axa, na, sa, xb, bb.shape[0], bb.shape[1],
+                           axb, nb, sb, h, mode)
+    torch.cuda.synchronize()
+    for (b, axis), (_, n, s), w in zip(bits, outs, "AB"):
+        on, os_ = O.quantize_chunked(b, axis, h, mode)
+        assert np.array_equal(n.cpu().numpy(), on), f"{w} nibbles {pair} h={h} mode={mode}"
+        assert np.array_equal(s.cpu().numpy(), os_), f"{w} scales {pair} h={h} mode={mode}"
