@@ -111,7 +111,7 @@ def test_tiny_fprop_workload_fp32_and_bf16():
 
 
 # --------------------------------------------------------------- full size
-def sampled_check(op, P, Q, T, N, K, h, mode, out_dtype, nsample=48, seed=0):
+def sampled_check(op, P, Q, T, N, K, h, mode, out_dtype, nsample=192, seed=0):
     C, ga, gb = run_fused(op, P, Q, T, N, K, h, mode, out_dtype)
     (GM, GN, GK) = operand_layout(op, T, N, K)[2]
     rng = np.random.default_rng(seed)

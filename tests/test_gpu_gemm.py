@@ -67,6 +67,9 @@ SHAPES = [
     # previous tile's k-loop prefetched
     (6448, 6504, 2048),  # 26 x 26 = 676 tiles, both edges ragged
     (4200, 4400, 4096),  # 17 x 18 = 306 tiles, the Llama reduction length
+    # 2 x 130 = 260 tiles on 256 compute units: four work-groups walk to a
+    # second tile; 33280 columns of output; ragged M
+    (500, 33280, 2048),
 ]
 
 
