@@ -49,14 +49,20 @@ def short(name: str) -> str:
 
 # The persistent GEMM launches one work-group per CU for every shape, so its
 # grid does not identify the product; the quantizer launch just before it
-# does (its B operand: grid = blocks of the weight or the column source).
-PRODUCT_OF_B_GRID = {786432: "qkv fprop (8192,6144,4096)",
+# does. Keys are grid sizes in threads: the two-operand launch of each
+# product (512 threads per work-group: A and B groups together), and the B
+# operand's own launch for runs that quantize the operands one by one.
+PRODUCT_OF_B_GRID = {(2048 + 1536) * 512: "qkv fprop (8192,6144,4096)",
+                     (2048 + 7168) * 512: "gate+up fprop (8192,28672,4096)",
+                     (2048 + 896) * 512: "down dgrad (8192,14336,4096)",
+                     (512 + 1792) * 512: "down wgrad (4096,14336,8192)",
+                     786432: "qkv fprop (8192,6144,4096)",
                      3670016: "gate+up fprop (8192,28672,4096)",
                      458752: "down dgrad (8192,14336,4096)",
                      917504: "down wgrad (4096,14336,8192)"}
 
 
-def trace_summary(path):
+def trace_summary(path, window=None):
     groups = defaultdict(list)
     with open(path) as f:
         rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
@@ -77,6 +83,27 @@ def trace_summary(path):
         med = sorted(d)[len(d) // 2]
         print(f"| {k} | {g} | {wg} | {len(d)} | {sum(d) / len(d):.2f} | {med:.2f} | {min(d):.2f} | "
               f"{max(d):.2f} |")
+    if window:
+        # bench.py's first GPU work is W warm-up steps, then K steps with an
+        # event around every launch: dispatches W .. W + K - 1 of each
+        # step kernel (in time order) are the ones its per-kernel means use
+        w, k = window
+        print()
+        print(f"Step launches only (dispatches {w} .. {w + k - 1} of each kernel and product, "
+              f"the bench's per-kernel pass):")
+        print()
+        print("| kernel | calls | avg us | median us | min us | max us |")
+        print("|---|---|---|---|---|---|")
+        for (name, g, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            if not (name.startswith("gemm_dma_kernel") and name.endswith("]") and ", 0>" in name
+                    or name.startswith("quant_pair_kernel")):
+                continue
+            sel = d[w:w + k]
+            if len(sel) < k:
+                continue
+            med = sorted(sel)[len(sel) // 2]
+            print(f"| {name} (grid {g}) | {len(sel)} | {sum(sel) / len(sel):.2f} | {med:.2f} | "
+                  f"{min(sel):.2f} | {max(sel):.2f} |")
 
 
 def pmc_summary(path):
@@ -228,6 +255,8 @@ def traffic(fetch_csv, write_csv, kernel_src, out_json):
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("trace", nargs="?")
+    ap.add_argument("--step-window", nargs=2, type=int, metavar=("W", "K"),
+                    help="also list dispatches W .. W+K-1 of each step kernel")
     ap.add_argument("--pmc")
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL_SRC", "OUT_JSON"))
     ap.add_argument("--traffic-md", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"))
@@ -235,7 +264,7 @@ if __name__ == "__main__":
     ap.add_argument("--command", default="", help="command line recorded in the markdown")
     a = ap.parse_args()
     if a.trace:
-        trace_summary(a.trace)
+        trace_summary(a.trace, a.step_window)
     if a.pmc:
         pmc_summary(a.pmc)
     if a.traffic:
