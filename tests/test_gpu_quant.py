@@ -47,7 +47,7 @@ SHAPES = {
     0: [(1, 32), (3, 96), (257, 160), (64, 4128), (256, 256), (96, 8192)],
     1: [(32, 1), (64, 7), (32, 100), (96, 520), (128, 1544), (160, 8), (256, 300), (384, 4),
         (128, 260)],
-    2: [(32, 32), (64, 96), (96, 320), (32, 4096)],
+    2: [(32, 32), (64, 96), (96, 320), (32, 4096), (64, 512), (96, 256)],
 }
 
 
@@ -98,6 +98,15 @@ def edge_matrix(rows=64, cols=128, seed=5):
 def test_edge_values_bit_exact(axis, h, mode):
     bits = edge_matrix()
     assert_same(bits, axis, h, mode, f"edge axis={axis} h={h} mode={mode}")
+
+
+@pytest.mark.parametrize("h", [0, 16, 32])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_edge_values_2d_lane_contiguous(h, mode):
+    """Edge blocks in 32x32 tiles whose column groups are whole 256-column
+    groups (the lane-contiguous 2D kernel)."""
+    bits = edge_matrix(96, 512, seed=9)
+    assert_same(bits, 2, h, mode, f"edge 2d 96x512 h={h} mode={mode}")
 
 
 def test_col_equals_row_of_transpose():
