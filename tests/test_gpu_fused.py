@@ -7,8 +7,10 @@ bit-exactly, and (2) the output against the oracle's fp64 GEMM of the
 oracle's dequantized operands (|C - C_ref| <= 1e-5 sum|a||b|, plus 2^-8
 |C_ref| for bf16 output). Small ragged shapes are checked in full; the four
 Llama-3.1-8B products at full size are checked on sampled output rows and
-columns, with the sampled operand rows quantized by the oracle from the
-matching source slices.
+columns for every rotation, rule and output type, with the sampled operand
+rows quantized by the oracle from the matching source slices; the QKV Fprop
+and the down-projection Wgrad are also checked on every output element and
+every operand byte.
 """
 import numpy as np
 import pytest
@@ -176,3 +178,32 @@ def test_down_wgrad_full_ceil(down_wgrad):
 
 def test_down_wgrad_full_bf16_out(down_wgrad):
     sampled_check("wgrad", down_wgrad["dY"], down_wgrad["X"], 8192, 4096, 14336, 16, 1, 1)
+
+
+def full_check(op, P, Q, T, N, K, h, mode, out_dtype):
+    """Every byte of both packed operands against the oracle's quantizer and
+    every output element against the oracle's fp64 product."""
+    import os
+    C, ga, gb = run_fused(op, P, Q, T, N, K, h, mode, out_dtype)
+    threads = max(1, len(os.sched_getaffinity(0)))
+    axa, axb = {"fprop": (0, 0), "dgrad": (0, 1), "wgrad": (1, 1)}[op]
+    qa = O.quantize_chunked(P, axa, h, mode, chunk=64, threads=threads)
+    qb = O.quantize_chunked(Q, axb, h, mode, chunk=64, threads=threads)
+    what = f"{op} T,N,K={(T, N, K)} h={h} mode={mode} every element"
+    for g, w, name in ((ga, qa, "A"), (gb, qb, "B")):
+        assert np.array_equal(g[0], w[0]), f"{what}: {name} nibbles"
+        assert np.array_equal(g[1], w[1]), f"{what}: {name} scales"
+    check_output(C, qa, qb, out_dtype == 1, what)
+
+
+def test_qkv_fprop_every_element(qkv):
+    """The QKV Fprop at full size (8192 x 6144 outputs, K = 4096): all 50 M
+    outputs and all operand bytes."""
+    full_check("fprop", qkv["X"], qkv["W"], 8192, 6144, 4096, 16, 0, 0)
+
+
+def test_down_wgrad_every_element(down_wgrad):
+    """The down-projection Wgrad at full size (4096 x 14336 outputs, the
+    8192-token reduction, both operands column-wise): all 59 M outputs and
+    all operand bytes."""
+    full_check("wgrad", down_wgrad["dY"], down_wgrad["X"], 8192, 4096, 14336, 16, 0, 0)
