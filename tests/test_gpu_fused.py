@@ -9,8 +9,8 @@ oracle's dequantized operands (|C - C_ref| <= 1e-5 sum|a||b|, plus 2^-8
 Llama-3.1-8B products at full size are checked on sampled output rows and
 columns for every rotation, rule and output type, with the sampled operand
 rows quantized by the oracle from the matching source slices; the QKV Fprop
-and the down-projection Wgrad are also checked on every output element and
-every operand byte.
+and the down-projection Dgrad and Wgrad are also checked on every output
+element and every operand byte.
 """
 import numpy as np
 import pytest
@@ -207,3 +207,10 @@ def test_down_wgrad_every_element(down_wgrad):
     8192-token reduction, both operands column-wise): all 59 M outputs and
     all operand bytes."""
     full_check("wgrad", down_wgrad["dY"], down_wgrad["X"], 8192, 4096, 14336, 16, 0, 0)
+
+
+def test_down_dgrad_every_element(mlp):
+    """The down-projection Dgrad at full size (8192 x 14336 outputs, K = 4096
+    along N, W quantized column-wise): all 117 M outputs and all operand
+    bytes."""
+    full_check("dgrad", mlp["dY"], mlp["W_down"], 8192, 4096, 14336, 16, 0, 0)
