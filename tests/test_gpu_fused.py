@@ -8,9 +8,9 @@ oracle's dequantized operands (|C - C_ref| <= 1e-5 sum|a||b|, plus 2^-8
 |C_ref| for bf16 output). Small ragged shapes are checked in full; the four
 Llama-3.1-8B products at full size are checked on sampled output rows and
 columns for every rotation, rule and output type, with the sampled operand
-rows quantized by the oracle from the matching source slices; the QKV Fprop
-and the down-projection Dgrad and Wgrad are also checked on every output
-element and every operand byte.
+rows quantized by the oracle from the matching source slices; with
+H16 and OCP floor scales all four are also checked on every output element
+and every operand byte.
 """
 import numpy as np
 import pytest
@@ -214,3 +214,9 @@ def test_down_dgrad_every_element(mlp):
     along N, W quantized column-wise): all 117 M outputs and all operand
     bytes."""
     full_check("dgrad", mlp["dY"], mlp["W_down"], 8192, 4096, 14336, 16, 0, 0)
+
+
+def test_gate_up_fprop_every_element(mlp):
+    """The MLP gate+up Fprop at full size (8192 x 28672 outputs, K = 4096):
+    all 235 M outputs and all operand bytes."""
+    full_check("fprop", mlp["X"], mlp["W_gu"], 8192, 28672, 4096, 16, 0, 0)
