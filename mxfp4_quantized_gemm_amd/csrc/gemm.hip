@@ -1088,6 +1088,26 @@ __device__ __forceinline__ void dma_data(uint8_t* st, const TileRes& T, const La
   for (int u = 0; u < G::DA; ++u) dma_b128(rb, st + TILE + (G::DA * wave + u) * 1024, L.d[u], ko);
 }
 
+// Half PART (0 or 1) of dma_data: the first or last DA / 2 blocks of each
+// operand. The pipeline issues a k-tile's two halves one k-step apart, which
+// spreads the TA work of the DMAs over two MFMA groups instead of one (about
+// 2 % faster on the Llama products than one burst; thirds or quarters were
+// slower).
+template <class G, int PART>
+__device__ __forceinline__ void dma_data_half(uint8_t* st, const TileRes& T, const Lane<G>& L,
+                                              int kt, bool live, rsrc_t none, int wave) {
+  static_assert(G::DA % 2 == 0, "DA must split in two halves");
+  const rsrc_t ra = live ? T.a : none, rb = live ? T.b : none;
+  const uint32_t ko = (uint32_t)kt * KB;
+  constexpr int H = G::DA / 2;
+#pragma unroll
+  for (int u = PART * H; u < (PART + 1) * H; ++u)
+    dma_b128(ra, st + (G::DA * wave + u) * 1024, L.d[u], ko);
+#pragma unroll
+  for (int u = PART * H; u < (PART + 1) * H; ++u)
+    dma_b128(rb, st + TILE + (G::DA * wave + u) * 1024, L.d[u], ko);
+}
+
 // Scale group g (k-tiles 4 g .. 4 g + 3) of the tile T into sg (A rows, then B rows).
 template <class G>
 __device__ __forceinline__ void dma_scales(uint8_t* sg, const TileRes& T, const Lane<G>& L, int g,
@@ -1190,9 +1210,10 @@ __device__ __forceinline__ void tile_at(int64_t vt, int64_t ntiles, int64_t ntm,
 // One k-tile k (C = k % 8) of the current tile, in stage C % 2; F0 / SCc
 // hold its k-step-0 fragments and its scales. The barrier before the last
 // k-step publishes k-tile k + 1 (every wave waited for its own DMAs of it)
-// and retires stage C % 2, which then receives k-tile k + 2 -- of the next
-// tile (Tn) when k + 2 runs past this tile -- while the last MFMAs of k-tile
-// k run. When C % 4 == 3 the scale group buffer of k-tiles k - 3 .. k is
+// and retires stage C % 2, which then receives the first half of k-tile
+// k + 2 -- of the next tile (Tn) when k + 2 runs past this tile -- while the
+// last MFMAs of k-tile k run; its second half follows with k-step 0 of k-tile
+// k + 1. When C % 4 == 3 the scale group buffer of k-tiles k - 3 .. k is
 // retired the same way and receives group (k + 5) / 4.
 template <class G, int C>
 __device__ __forceinline__ void ktile(uint8_t* st0, uint8_t* st1, uint8_t* sg0, uint8_t* sg1,
@@ -1209,7 +1230,12 @@ __device__ __forceinline__ void ktile(uint8_t* st0, uint8_t* st1, uint8_t* sg0, 
   uint8_t* sgw = (((C + 5) >> 2) & 1) ? sg1 : sg0;  // group (k + 5) / 4, written when SG
   read_frags<G, 1>(cur, ra, F1);
   mfma_ab<TM, TN, 0>(F0, SCc, acc);
-  lt::interleave<0, NM, NR, 0, 0>();
+  {  // second half of k-tile k + 1
+    const int kk = k + 1;
+    const bool nx = kk >= nkt;
+    dma_data_half<G, 1>(nxt, nx ? Tn : Tc, L, nx ? kk - nkt : kk, nx ? has_next : true, none, wave);
+  }
+  lt::interleave<0, NM, NR, 0, G::NDMA / 2>();
   __builtin_amdgcn_sched_barrier(0);
   read_frags<G, 2>(cur, ra, F0);
   mfma_ab<TM, TN, 1>(F1, SCc, acc);
@@ -1226,7 +1252,7 @@ __device__ __forceinline__ void ktile(uint8_t* st0, uint8_t* st1, uint8_t* sg0, 
   {
     const int kk = k + 2;
     const bool nx = kk >= nkt;
-    dma_data<G>(cur, nx ? Tn : Tc, L, nx ? kk - nkt : kk, nx ? has_next : true, none, wave);
+    dma_data_half<G, 0>(cur, nx ? Tn : Tc, L, nx ? kk - nkt : kk, nx ? has_next : true, none, wave);
   }
   if constexpr (SG) {
     const int g = (k + 5) >> 2, ng = nkt >> 2;
@@ -1234,7 +1260,7 @@ __device__ __forceinline__ void ktile(uint8_t* st0, uint8_t* st1, uint8_t* sg0, 
     dma_scales<G>(sgw, nx ? Tn : Tc, L, nx ? g - ng : g, nx ? has_next : true, none, wave);
   }
   mfma_ab<TM, TN, 3>(F1, SCc, acc);
-  lt::interleave<0, NM, 2 * NR, 0, G::NDMA + (SG ? 2 * G::DS : 0)>();
+  lt::interleave<0, NM, 2 * NR, 0, G::NDMA / 2 + (SG ? 2 * G::DS : 0)>();
   // the scale byte gathers (v_perm) wait for their reads: keep them last
   __builtin_amdgcn_sched_group_barrier(0x002, NR, 0);
   __builtin_amdgcn_sched_barrier(0);
@@ -1278,16 +1304,17 @@ void gemm_dma_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   if (has_next) tile_at(vt + P, ntiles, ntm, ntn, m0n, n0n);
   tile_res(Tn, A, As, B, Bs, m0n, n0n, M, N, kbytes, kblk);
 
-  // Prologue: scale group 0, k-tiles 0 and 1, scale group 1 (nkt % 8 == 0).
-  // Loads complete in issue order, so this wave's DMAs of group 0 and k-tile
-  // 0 have landed once at most NDMA + 2 DS are outstanding. No LDS reads
-  // precede this barrier, so it needs no release fence (which would also wait
-  // for the later DMAs); the acquire fence keeps the reads below it.
+  // Prologue: scale group 0, k-tile 0, the first half of k-tile 1 (k-tile 0
+  // issues the second), scale group 1 (nkt % 8 == 0). Loads complete in
+  // issue order, so this wave's DMAs of group 0 and k-tile 0 have landed once
+  // at most NDMA / 2 + 2 DS are outstanding. No LDS reads precede this
+  // barrier, so it needs no release fence (which would also wait for the
+  // later DMAs); the acquire fence keeps the reads below it.
   dma_scales<G>(sg0, Tc, L, 0, true, none, wave);
   dma_data<G>(st0, Tc, L, 0, true, none, wave);
-  dma_data<G>(st1, Tc, L, 1, true, none, wave);
+  dma_data_half<G, 0>(st1, Tc, L, 1, true, none, wave);
   dma_scales<G>(sg1, Tc, L, 1, true, none, wave);
-  wait_vm<G::NDMA + 2 * G::DS>();
+  wait_vm<G::NDMA / 2 + 2 * G::DS>();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   lt::Frag<TM, TN> F0, F1;
