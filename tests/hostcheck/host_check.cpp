@@ -183,7 +183,7 @@ void gemm_cases() {
   CHECK(stub::g_calls[0].i[0] == 1 && stub::g_calls[0].i[1] == 1);
 }
 
-// One fused product: the two quantize launches and the GEMM, with the
+// One fused product: the two-operand quantize launch and the GEMM, with the
 // workspace carved as A nibbles | A scales | B nibbles | B scales, each part
 // rounded up to 256 bytes.
 void fused_case(int op, int64_t T, int64_t N, int64_t K) {
