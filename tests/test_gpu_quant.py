@@ -245,6 +245,7 @@ PAIRS = [
     (((64, 256), 0), ((512, 260), 1)),        # row + column (8-band staged)
     (((256, 100), 1), ((768, 36), 1)),        # column + column
     (((512, 64), 1), ((4096, 8320), 0)),      # column + lane-contiguous row
+    (((4096, 8320), 0), ((512, 260), 1)),     # lane-contiguous row + column (column runs first)
     (((96, 64), 1), ((64, 96), 0)),           # column shape without the staged form: two launches
 ]
 
