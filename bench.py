@@ -17,8 +17,9 @@ HBM when the timed region starts. The timed region is K steps launched
 back to back with nothing else on the stream; `value` is the step's total
 2MNK over its wall time. A second pass of K steps brackets every launch
 with HIP events on the launch stream, giving per-kernel average durations
-(the roofline figure). The fused entry points are timed as well (same
-kernels), right after the timed region, as a cross-check.
+(the roofline figure). The fused entry points, and the step captured in a
+HIP graph and replayed, are timed as well (same kernels), right after the
+timed region, as cross-checks.
 
 Also measured: the quantizer-only workload (8192 x 4096, Student-t x
 log-normal) for every axis and scale rule with H16, plus H0/H32 row-wise,
@@ -397,15 +398,16 @@ def main():
                            device=dev),
         ))
 
-    def launches(p, mode=0):
+    def launches(p, mode=0, st=None):
         # both operands in one launch (mxfp4_quantize_pair), then the GEMM:
         # the launches mxfp4_fprop / dgrad / wgrad issue
+        st = stream if st is None else st
         return [
             lambda: mx.mxfp4_quantize_pair(p["P"], p["sa"][0], p["sa"][1], p["axa"], p["an"],
                                            p["asc"], p["Q"], p["sb"][0], p["sb"][1], p["axb"],
-                                           p["bn"], p["bsc"], 16, mode, stream),
+                                           p["bn"], p["bsc"], 16, mode, st),
             lambda: mx.mxfp4_gemm(p["an"], p["asc"], p["bn"], p["bsc"], p["GM"], p["GN"], p["GK"],
-                                  p["C"], mx.OUT_F32, stream),
+                                  p["C"], mx.OUT_F32, st),
         ]
 
     seq = [(p, j, fn) for p in prods for j, fn in enumerate(launches(p))]
@@ -710,6 +712,26 @@ def main():
     torch.cuda.synchronize()
     fused_ms = (time.perf_counter() - t_f) * 1e3 / K_
 
+    # the same step captured once in a HIP graph (the library allocates and
+    # synchronizes nothing, so its launches are capturable) and replayed K
+    # times: a cross-check that host launch overhead is not in the headline
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side), torch.cuda.graph(graph, stream=side):
+        for p in prods:
+            for fn in launches(p, 0, side):
+                fn()
+    stream.wait_stream(side)
+    graph.replay()
+    torch.cuda.synchronize()
+    t_g = time.perf_counter()
+    for _ in range(K_):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t_g) * 1e3 / K_
+    del graph
+
     # -------------------------------------------------------------- roofline
     dom = [k for k in kernels if k["kernel"] == f"{DOMINANT}.gemm"][0]
     dp = [p for p in prods if p["name"] == DOMINANT][0]
@@ -743,6 +765,7 @@ def main():
         "products": per_product,
         "event_ms_per_step": round(event_ms_per_step, 4),
         "fused_entry_ms_per_step": round(fused_ms, 4),
+        "graph_replay_ms_per_step": round(graph_ms, 4),
         "ceil_scales_ms_per_step": round(ceil_ms_per_step, 4),
         "ceil_scales_TFLOP/s": round(total_flops / (ceil_ms_per_step * 1e-3) / 1e12, 2),
         "kernels": kernels,
