@@ -198,6 +198,61 @@ def test_error_stats_validation(lib):
     assert es(lib, out=ctypes.c_void_p(0x10004)) == 6
 
 
+def test_error_stats_noalloc_validation(lib):
+    call = lambda **kw: lib.mxfp4_error_stats_noalloc(
+        kw.get("src", FAKE), kw.get("rows", 64), kw.get("cols", 64), kw.get("axis", 0),
+        kw.get("h", 16), kw.get("mode", 0), kw.get("out", FAKE), NULL)
+    assert call(axis=2) == 3
+    assert call(h=8) == 3
+    assert call(mode=2) == 3
+    assert call(cols=48) == 2
+    assert call(axis=1, rows=48) == 2
+    assert call(src=NULL) == 1
+    assert call(out=NULL) == 1
+    assert call(src=FAKE_ODD) == 6
+    assert call(out=ctypes.c_void_p(0x10004)) == 6
+
+
+def qp(lib, a=(FAKE, 64, 64, 0, FAKE, FAKE), b=(FAKE, 64, 64, 1, FAKE, FAKE), h=16, mode=0):
+    return lib.mxfp4_quantize_pair(*a, *b, h, mode, NULL)
+
+
+def test_quantize_pair_validation(lib):
+    """Each operand is validated as by mxfp4_quantize, operand A's errors
+    first; 2D blocks are not a pair axis."""
+    A, B = (FAKE, 64, 64, 0, FAKE, FAKE), (FAKE, 64, 64, 1, FAKE, FAKE)
+    with_ = lambda t, i, v: tuple(v if k == i else x for k, x in enumerate(t))
+    assert qp(lib, a=with_(A, 3, 2)) == 3
+    assert qp(lib, b=with_(B, 3, 2)) == 3
+    assert qp(lib, h=8) == 3
+    assert qp(lib, mode=2) == 3
+    assert qp(lib, a=with_(A, 2, 48)) == 2            # A row axis: cols % 32
+    assert qp(lib, b=with_(B, 1, 48)) == 2            # B column axis: rows % 32
+    assert qp(lib, a=with_(A, 0, NULL)) == 1
+    assert qp(lib, b=with_(B, 4, NULL)) == 1
+    assert qp(lib, b=with_(B, 0, FAKE_ODD)) == 6
+    # A's error is reported when both operands are invalid
+    assert qp(lib, a=with_(A, 2, 48), b=with_(B, 0, NULL)) == 2
+    assert qp(lib, a=with_(A, 0, NULL), b=with_(B, 1, 48)) == 1
+    # two empty operands are valid and launch nothing, even with NULL buffers
+    assert qp(lib, a=(NULL, 0, 64, 0, NULL, NULL), b=(NULL, 64, 0, 1, NULL, NULL)) == 0
+
+
+def test_gemm_mbs_validation(lib):
+    call = lambda **kw: lib.mxfp4_gemm_mbs(
+        kw.get("A", FAKE), kw.get("As", FAKE), kw.get("Am", FAKE), kw.get("B", FAKE),
+        kw.get("Bs", FAKE), kw.get("Bm", FAKE), kw.get("M", 64), kw.get("N", 64),
+        kw.get("K", 128), kw.get("C", FAKE), kw.get("out", 0), NULL)
+    assert call(out=2) == 3
+    assert call(M=0) == 2
+    assert call(K=96) == 2                     # K % 128 (one 8-bit mantissa per 128 k)
+    assert call(K=48) == 2
+    assert call(A=NULL) == 1
+    assert call(Am=NULL) == 1
+    assert call(Bm=NULL) == 1
+    assert call(C=ctypes.c_void_p(0x10002)) == 6
+
+
 def g(lib, M=64, N=64, K=64, out=0, A=FAKE, As=FAKE, B=FAKE, Bs=FAKE, C=FAKE):
     return lib.mxfp4_gemm(A, As, B, Bs, M, N, K, C, out, NULL)
 
