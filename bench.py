@@ -398,14 +398,14 @@ def main():
                            device=dev),
         ))
 
-    def launches(p, mode=0, st=None):
+    def launches(p, mode=0, st=None, h=16):
         # both operands in one launch (mxfp4_quantize_pair), then the GEMM:
         # the launches mxfp4_fprop / dgrad / wgrad issue
         st = stream if st is None else st
         return [
             lambda: mx.mxfp4_quantize_pair(p["P"], p["sa"][0], p["sa"][1], p["axa"], p["an"],
                                            p["asc"], p["Q"], p["sb"][0], p["sb"][1], p["axb"],
-                                           p["bn"], p["bsc"], 16, mode, st),
+                                           p["bn"], p["bsc"], h, mode, st),
             lambda: mx.mxfp4_gemm(p["an"], p["asc"], p["bn"], p["bsc"], p["GM"], p["GN"], p["GK"],
                                   p["C"], mx.OUT_F32, st),
         ]
@@ -485,6 +485,34 @@ def main():
         rec["gemm_bf16_out_us"] = round(us, 2)
         rec["gemm_bf16_out_TFLOPs"] = round(2.0 * p["GM"] * p["GN"] * p["GK"] / (us * 1e-6) / 1e12, 1)
         del cb
+
+    # the step with H0 and H32 instead of H16 (the comparison arms of the
+    # rotation), K steps with an event around every launch as in the pass
+    # above: each product's two-operand quantize launch in its place in the
+    # step, and the fused TFLOP/s with that step's GEMM time
+    for h in (0, 32):
+        seq_h = [fn for p in prods for fn in launches(p, 0, None, h)]
+        for fn in seq_h:
+            fn()
+        evh = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq_h) + 1)]
+               for _ in range(K_)]
+        for s_ in range(K_):
+            evh[s_][0].record(stream)
+            for i, fn in enumerate(seq_h):
+                fn()
+                evh[s_][i + 1].record(stream)
+        torch.cuda.synchronize()
+        Dh = np.array([[evh[s_][i].elapsed_time(evh[s_][i + 1]) for i in range(len(seq_h))]
+                       for s_ in range(K_)]).mean(axis=0) * 1e3
+        for k, p in enumerate(prods):
+            rec = per_product[p["name"]]
+            b = (quant_bytes(p["sa"][0], p["sa"][1], p["axa"]) +
+                 quant_bytes(p["sb"][0], p["sb"][1], p["axb"]))
+            qu, gu = Dh[2 * k], Dh[2 * k + 1]
+            rec[f"quant_AB_h{h}_us"] = round(qu, 2)
+            rec[f"quant_AB_h{h}_GBs"] = round(b / (qu * 1e-6) / 1e9, 1)
+            rec[f"fused_h{h}_TFLOPs"] = round(2.0 * p["GM"] * p["GN"] * p["GK"] /
+                                              ((qu + gu) * 1e-6) / 1e12, 1)
 
     # -------------------------------------------------- quantizer workload
     quant = None
