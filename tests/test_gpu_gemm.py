@@ -121,3 +121,31 @@ def test_gemm_deterministic():
     c1 = run_gemm(a, b, M, N, K)
     c2 = run_gemm(a, b, M, N, K)
     assert np.array_equal(c1, c2)
+
+
+def test_gemm_operand_beyond_4gib():
+    """An A operand of 4 GiB + 1 MiB (2^21 + 512 rows of 2048 bytes, K = 4096)
+    takes the general kernel with 64-bit offsets (the large-tile kernels
+    address operands with 32-bit offsets). Rows on both sides of byte
+    offset 2^32 are checked against the oracle on every output column."""
+    import torch
+    import mxfp4_quantized_gemm_amd as mx
+    M, N, K = (1 << 21) + 512, 128, 4096
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4242)
+    A = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device="cuda", generator=g)
+    As = torch.randint(120, 135, (M, K // 32), dtype=torch.uint8, device="cuda", generator=g)
+    b = random_operand(N, K, 77, 120, 134)
+    B, Bs = to_dev_u8(b[0]), to_dev_u8(b[1])
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    mx.mxfp4_gemm(A, As, B, Bs, M, N, K, C, mx.OUT_F32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, 1, 1 << 20, (1 << 21) - 1, 1 << 21, (1 << 21) + 1, M - 1],
+                                     rng.integers(0, M, 24)]))
+    idx = torch.from_numpy(rows).to("cuda")
+    a = (A[idx].cpu().numpy(), As[idx].cpu().numpy())
+    got = C[idx].cpu().numpy().astype(np.float64)
+    del A, As, C
+    torch.cuda.empty_cache()
+    check(got, a, b, what=f"A of {M * K // 2} bytes, rows {rows.tolist()}")
