@@ -297,6 +297,20 @@ def test_fused_validation(lib, name):
     assert call(ws=ctypes.c_void_p(0x10010)) == 6   # workspace must be 256 B aligned
 
 
+def test_linear_wrapper_validates_and_never_computes_on_the_cpu():
+    """MXFP4Linear checks its sizes, and a CPU tensor is rejected by the
+    binding before any call (there is no CPU path)."""
+    import torch
+    from mxfp4_quantized_gemm_amd.linear import MXFP4Linear
+    with pytest.raises(ValueError):
+        MXFP4Linear(48, 64)
+    layer = MXFP4Linear(64, 32)
+    with pytest.raises(ValueError):
+        layer(torch.zeros(16, 64, dtype=torch.bfloat16))      # 16 rows: not a multiple of 32
+    with pytest.raises(ValueError, match="GPU memory"):
+        layer(torch.zeros(32, 64, dtype=torch.bfloat16))
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     saved = mx._LIB
     try:
