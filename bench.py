@@ -100,7 +100,7 @@ def load_traffic(kernel_src):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(work, budget_rows=2048, budget_cols=8192):
+def cpu_baseline(work, budget_rows=8192, budget_cols=16384):
     """Oracle on a bounded sample of the step: for each product, a
     budget_rows x budget_cols tile of the output at full reduction length
     (quantize the matching source slices, dequantize, fp64 GEMM + sum|a||b|)."""
