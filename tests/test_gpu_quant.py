@@ -272,3 +272,52 @@ def test_pair_launch_bit_exact(pair, h, mode):
         on, os_ = O.quantize_chunked(b, axis, h, mode)
         assert np.array_equal(n.cpu().numpy(), on), f"{w} nibbles {pair} h={h} mode={mode}"
         assert np.array_equal(s.cpu().numpy(), os_), f"{w} scales {pair} h={h} mode={mode}"
+
+
+@pytest.mark.parametrize("axis", [0, 1, 2])
+def test_source_beyond_4gib(axis):
+    """A bf16 source of 4 GiB + 16 MiB (65792 x 32768, more than 2^31
+    elements; the lane-contiguous row, the staged column and the
+    lane-contiguous 2D kernels): blocks on both sides of element 2^31
+    against the oracle, row blocks by whole rows, column blocks by 32-row
+    bands of sampled columns, 2D tiles by sampled tiles."""
+    import torch
+    import mxfp4_quantized_gemm_amd as mx
+    rows, cols = 65536 + 256, 32768
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77 + axis)
+    x = torch.randn((rows, cols), dtype=torch.float32, device="cuda", generator=g)
+    x = x.to(torch.bfloat16)
+    nib, sc = mx.quantize(x, axis, 16, 0)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(axis)
+    edge_rows = [0, 65535, 65536, rows - 1]             # row 65536 starts at element 2^31
+
+    def src(r0, r1, c0, c1):
+        return x[r0:r1, c0:c1].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    if axis == 0:
+        for r in edge_rows + rng.integers(0, rows, 4).tolist():
+            on, os_ = O.quantize(src(r, r + 1, 0, cols), O.AXIS_ROW, 16, 0)
+            assert np.array_equal(nib[r:r + 1].cpu().numpy(), on), f"row {r} nibbles"
+            assert np.array_equal(sc[r:r + 1].cpu().numpy(), os_), f"row {r} scales"
+    else:
+        cs = sorted(set([0, cols - 1] + rng.integers(0, cols, 30).tolist()))
+        for r in edge_rows:
+            b = r // 32
+            for c in cs[:8] if axis == 2 else [0]:
+                if axis == 1:
+                    blk = src(32 * b, 32 * b + 32, 0, cols)[:, cs]
+                    on, os_ = O.quantize(np.ascontiguousarray(blk), O.AXIS_COL, 16, 0)
+                    got_n = nib[cs, 16 * b:16 * b + 16].cpu().numpy()
+                    got_s = sc[cs, b:b + 1].cpu().numpy()
+                else:
+                    t = c // 32
+                    on, os_ = O.quantize(src(32 * b, 32 * b + 32, 32 * t, 32 * t + 32),
+                                         O.AXIS_2D, 16, 0)
+                    got_n = nib[32 * b:32 * b + 32, 16 * t:16 * t + 16].cpu().numpy()
+                    got_s = sc[b:b + 1, t:t + 1].cpu().numpy()
+                assert np.array_equal(got_n, on), f"axis {axis} band {b} col {c} nibbles"
+                assert np.array_equal(got_s, os_), f"axis {axis} band {b} col {c} scales"
+    del x, nib, sc
+    torch.cuda.empty_cache()
