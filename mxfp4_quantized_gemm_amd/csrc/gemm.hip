@@ -30,6 +30,7 @@
 // before the MFMAs of tile k and written to the other buffer after them,
 // with one barrier per k-tile.
 #include <hip/hip_runtime.h>
+#include <atomic>
 #include <stdint.h>
 
 #include "internal.h"
@@ -965,7 +966,8 @@ hipError_t launch(const uint8_t* a, const uint8_t* as, const uint8_t* b, const u
 //  * buffer_load_dwordx4 ... lds: the 64 lanes of one instruction write 1 KiB
 //    of LDS at M0 + 16 lane, with no staging registers and no ds_write issued
 //    by the waves that run the MFMAs. A k-tile is 32 such blocks per operand
-//    (8 rows of 128 bytes each), 4 per wave;
+//    (8 rows of 128 bytes each), 4 per wave, issued in two halves one k-step
+//    apart;
 //  * the operand stream does not stop at tile boundaries: the last k-tiles of
 //    one tile prefetch the first k-tiles (and scale groups) of the next, so
 //    no tile starts with an exposed load, and no work-group is relaunched;
@@ -1423,15 +1425,21 @@ void gemm_dma_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ 
   wait_vm<0>();
 }
 
+// Compute units of the current device (the persistent grid), queried once
+// per device; calls from several host threads are safe.
 int cu_count() {
-  static int n = 0;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
   if (n == 0) {
-    int dev = 0, c = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
-      n = c;
-    else
-      n = 256;
+    int c = 0;
+    n = (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+         c > 0)
+            ? c
+            : 256;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
   return n;
 }
