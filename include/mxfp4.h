@@ -33,8 +33,10 @@
  *  - Pointers handed to vector loads/stores must be 16-byte aligned
  *    (bf16 sources, nibble outputs, GEMM operands); scale arrays and C need
  *    no alignment beyond their element size.
- *  - Calls are thread-safe (no global state); concurrent calls on one stream
- *    run in stream order.
+ *  - Calls are thread-safe. The only state shared between calls is a
+ *    per-device cache of the compute-unit count (set once, atomically) and
+ *    the static array of mxfp4_error_stats_noalloc (see there). Calls on
+ *    one stream run in stream order.
  */
 #ifndef MXFP4_H_
 #define MXFP4_H_
