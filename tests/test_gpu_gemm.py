@@ -70,6 +70,8 @@ SHAPES = [
     # 2 x 130 = 260 tiles on 256 compute units: four work-groups walk to a
     # second tile; 33280 columns of output; ragged M
     (500, 33280, 2048),
+    # the general kernel (K % 256 != 0) over 16 x 24 = 384 tiles, ragged
+    (2000, 3000, 800),
 ]
 
 
