@@ -88,7 +88,7 @@ def _check_mbs_product(C, a, b, out_bf16, what):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (130, 70, 128), (33, 257, 384), (200, 300, 640),
-                                   (256, 384, 4096), (300, 129, 1152)])
+                                   (256, 384, 4096), (300, 129, 1152), (1100, 1300, 2048)])
 @pytest.mark.parametrize("out_dtype", [0, 1])
 def test_gemm_mbs_random_operands(M, N, K, out_dtype):
     """Every nibble code and mantissa byte; K % 256 == 128 leaves the last
